@@ -1,0 +1,132 @@
+"""Planted mistakes in the oracle must be caught by the pins.
+
+Each mutant swaps one internal step of the CPU oracle for a plausible wrong
+version (a dropped cell type, a wrong sign, a wrong corner, a strict
+comparison, a shifted prefix sum, a transposed axis) and checks that the
+brute-force / topology pins reject it.  Mistakes are planted only in the
+oracle, on the CPU.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import ecc as oecc
+from tests import pins
+
+_real_cell_values = oecc.cell_values
+_real_first_k = oecc.first_k_bins
+
+
+def _cells_mutant(kind):
+    def gen(grid):
+        grid = np.asarray(grid)
+        cells = list(_real_cell_values(grid))
+        exts = [e for e in itertools.product((0, 1), repeat=grid.ndim)
+                if min(n - x for n, x in zip(grid.shape, e)) > 0]
+        for (val, dim), ext in zip(cells, exts):
+            if kind == "drop_top" and dim == grid.ndim:
+                continue
+            if kind == "edge_sign" and dim == 1:
+                yield val, 0
+                continue
+            if kind == "min_not_max" and dim == 1:
+                # an edge valued by its lower corner
+                anchors = [n - e for n, e in zip(grid.shape, ext)]
+                a = grid[tuple(slice(0, s) for s in anchors)]
+                b = grid[tuple(slice(e, e + s) for e, s in zip(ext, anchors))]
+                yield np.minimum(a, b), dim
+                continue
+            if kind == "square_misses_corner" and dim == 2:
+                # a square valued without its far corner
+                anchors = [n - e for n, e in zip(grid.shape, ext)]
+                axes = [i for i, e in enumerate(ext) if e]
+                v = grid[tuple(slice(0, s) for s in anchors)]
+                for ax in axes:
+                    off = [0] * grid.ndim
+                    off[ax] = 1
+                    v = np.maximum(v, grid[tuple(slice(o, o + s) for o, s in zip(off, anchors))])
+                yield v, dim
+                continue
+            if kind == "transposed" and dim == 1 and ext[-1] == 0:
+                # edges along another axis valued with the x neighbour (swapped axis)
+                if grid.shape[-1] > 1:
+                    yield np.maximum(grid[..., :-1], grid[..., 1:]), dim
+                continue
+            yield val, dim
+    return gen
+
+
+def _strict_bins(values, tau):
+    t = np.asarray(tau).astype(np.float32).astype(np.float64)
+    return np.searchsorted(t, np.asarray(values, np.float64).ravel(), side="right").astype(np.int64)
+
+
+def _run_pins():
+    """Return True if every pin passes for the currently patched oracle."""
+    rng = np.random.default_rng(1234)
+    try:
+        for ndim in (2, 3):
+            for _ in range(12):
+                shape = tuple(int(s) for s in rng.integers(2, 6, size=ndim))
+                g = rng.integers(0, 4, size=shape).astype(np.float32)
+                tau = np.array([-1, 0, 1, 2, 3, 4], np.float32)
+                got = oracle.ecc_hard(g, tau)
+                if got.tolist() != [pins.brute_chi(g, float(t)) for t in tau]:
+                    return False
+                for t in (0.0, 1.0, 2.0):
+                    if oracle.ecc_at(g, t) != pins.brute_chi(g, t):
+                        return False
+        for _ in range(12):
+            g = rng.integers(0, 3, size=(5, 7)).astype(np.float32)
+            for t in (0.0, 1.0):
+                b0, b1 = pins.betti_2d(g, t)
+                if oracle.ecc_at(g, t) != b0 - b1:
+                    return False
+    except Exception:
+        return False
+    return True
+
+
+def test_unpatched_oracle_passes_pins():
+    assert _run_pins()
+
+
+@pytest.mark.parametrize("kind", ["drop_top", "edge_sign", "min_not_max", "square_misses_corner", "transposed"])
+def test_cell_mutants_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(oecc, "cell_values", _cells_mutant(kind))
+    assert not _run_pins()
+
+
+def test_strict_comparison_is_caught(monkeypatch):
+    monkeypatch.setattr(oecc, "first_k_bins", _strict_bins)
+    assert not _run_pins()
+
+
+def test_shifted_prefix_sum_is_caught(monkeypatch):
+    real = oecc.ecc_hard
+
+    def shifted(grid, tau, slab=32):
+        e = real(grid, tau, slab)
+        return np.concatenate([[0], e[:-1]])
+
+    monkeypatch.setattr(oracle, "ecc_hard", shifted)
+    assert not _run_pins()
+
+
+def test_soft_sign_mutant_is_caught(monkeypatch):
+    """A soft oracle that drops the sign of edges fails the constant-grid closed form."""
+    def bad_grouped(grid, slab=32):
+        u, w = [], []
+        for val, dim in _real_cell_values(grid):
+            u.append(val.astype(np.float64).ravel())
+            w.append(np.ones(val.size, np.int64))
+        return np.concatenate(u), np.concatenate(w)
+
+    monkeypatch.setattr(oecc, "_grouped_weights", bad_grouped)
+    g = np.full((3, 4), 0.5, np.float32)
+    tau = np.array([0.25, 0.5, 0.75], np.float32)
+    want = [pins._sig(10.0 * (float(t) - 0.5)) for t in tau]
+    assert not np.allclose(oracle.ecc_soft(g, tau, 10.0), want)
