@@ -1,0 +1,24 @@
+"""Euler characteristic curves of dense 2D/3D grids on AMD Instinct MI355X.
+
+The compute path is libecc_mi355.so (hand-written HIP for gfx950, C ABI in
+include/ecc.h); ``euler_characteristic_curves_amd.ecc`` is its thin PyTorch
+binding.  The binding is imported lazily so that ``workloads`` (seeded
+synthetic inputs) can be used without the built library; any attempt to use
+an ECC entry point without the library raises ImportError.
+"""
+
+__version__ = "0.1.0"
+
+_API = (
+    "ecc_hard_2d", "ecc_hard_3d", "ecc_hard", "ecc_soft_fwd", "ecc_soft_bwd_tau",
+    "workspace_bytes", "get_workspace", "EccError", "SoftECC", "soft_ecc",
+)
+
+__all__ = list(_API)
+
+
+def __getattr__(name):
+    if name in _API:
+        from . import ecc as _ecc
+        return getattr(_ecc, name)
+    raise AttributeError(name)

@@ -1,0 +1,115 @@
+// Device-side building blocks shared by the hard and soft ECC kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ecc_internal.hpp"
+
+namespace ecc {
+
+// ---------------------------------------------------------------- atomics
+__device__ __forceinline__ long long agent_load(const long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void agent_store(long long* p, long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void agent_add(long long* p, long long v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Completion ticket: every workgroup calls this once after its global
+// atomics; exactly one (the last to arrive) gets true.  The ticket is reset
+// to zero by that workgroup so the workspace is clean for the next call.
+__device__ __forceinline__ bool last_block_arrives(unsigned int* ticket, int* lds_flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned int prev =
+        __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    int last = (prev == gridDim.x - 1);
+    if (last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = last;
+  }
+  __syncthreads();
+  bool last = *lds_flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+// --------------------------------------------------------- block scans
+// Inclusive scan of n values with kBlock threads, each thread owning one
+// contiguous segment.  `get(i)` produces element i (called twice per
+// element), `put(i, v)` receives the inclusive scan.  `tmp` holds kBlock T.
+template <typename T, typename Op, typename Get, typename Put>
+__device__ void block_scan(int n, T identity, Op op, Get get, Put put, T* tmp) {
+  const int t = threadIdx.x;
+  const int seg = (n + kBlock - 1) / kBlock;
+  const int b = t * seg;
+  const int e = min(b + seg, n);
+  T s = identity;
+  for (int i = b; i < e; ++i) s = op(s, get(i));
+  tmp[t] = s;
+  __syncthreads();
+  for (int off = 1; off < kBlock; off <<= 1) {
+    T v = t >= off ? tmp[t - off] : identity;
+    __syncthreads();
+    tmp[t] = op(tmp[t], v);
+    __syncthreads();
+  }
+  T run = t ? tmp[t - 1] : identity;
+  for (int i = b; i < e; ++i) {
+    run = op(run, get(i));
+    put(i, run);
+  }
+  __syncthreads();
+}
+
+// Running maximum of the thresholds: R_k = max(tau_0..tau_k) with fmaxf, so a
+// NaN threshold never admits a value.  min{k : v <= tau_k} equals
+// min{k : v <= R_k}, and R is non-decreasing, which makes binning a search.
+__device__ __forceinline__ void running_max_to_lds(const float* tau, int H, float* R, float* tmp) {
+  block_scan<float>(
+      H, -__builtin_inff(), [](float a, float b) { return fmaxf(a, b); },
+      [&](int i) { return tau[i]; }, [&](int i, float v) { R[i] = v; }, tmp);
+}
+
+// First k with v <= R[k] (R non-decreasing, in LDS), or H.  Exact fp32
+// comparisons; the linear guess only picks the starting point.
+__device__ __forceinline__ int bin_of(float v, const float* R, int H, float r0, float scale) {
+  float g = (v - r0) * scale;
+  g = fminf(fmaxf(g, 0.0f), (float)(H - 1));  // NaN guess -> 0
+  int k = (int)g;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    if (k > 0 && !(R[k - 1] < v)) --k;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    if (k < H && !(v <= R[k])) ++k;
+  const bool ok = (k == 0 || R[k - 1] < v) && (k == H || v <= R[k]);
+  if (!ok) {
+    int lo = 0, hi = H;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (v <= R[mid]) hi = mid; else lo = mid + 1;
+    }
+    k = lo;
+  }
+  return k;
+}
+
+// Linear-guess parameters for bin_of, from the running max in LDS.
+__device__ __forceinline__ void guess_params(const float* R, int H, float* r0, float* scale) {
+  const float a = R[0], b = R[H - 1];
+  float s = 0.0f;
+  if (H > 1) {
+    const float span = b - a;
+    if (span > 0.0f && span < __builtin_inff()) s = (float)(H - 1) / span;
+  }
+  if (!(s < __builtin_inff())) s = 0.0f;
+  *r0 = a;
+  *scale = s;
+}
+
+}  // namespace ecc

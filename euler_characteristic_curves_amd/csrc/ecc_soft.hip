@@ -1,0 +1,299 @@
+// Soft (sigmoid-relaxed) Euler characteristic curve and its threshold
+// gradient, gfx950.
+//
+// Method: page "Scalable GPU-Accelerated Euler Characteristic Curves"
+// (paper notes), "Method / Key designs / differentiable ECC layer": the hard
+// indicator of value <= tau becomes sigmoid(lambda (tau - value)), giving
+//     S_k   = sum_c (-1)^dim(c) s(lambda (tau_k - v_c)),
+//     dS/dtau_k = lambda sum_c (-1)^dim(c) s(x)(1 - s(x)),
+// evaluated by custom forward / backward kernels.  Cells and values are those
+// of the hard curve (max of corners, V-construction).
+//
+// Work split (cells x thresholds).  Each workgroup takes tiles of 1024 voxels.
+// Phase A turns a tile into a short list of (value, weight) terms: the same
+// exact regrouping as the hard kernels (four row sequences per voxel,
+// telescoped along x, equal values merged), so a term carries the summed sign
+// of every cell that has that value.  Phase B sweeps the list in LDS against
+// the thresholds: every lane owns 4 thresholds per 256-threshold chunk and
+// every wave a quarter of the terms.  The sigmoid costs one FMA and one
+// reciprocal per (term, threshold) in the factored form
+//     exp(lambda (v - tau)) = 2^{L (v - c)} * 2^{L (c - tau)},  L = lambda log2 e,
+// with the first factor computed once per term and the second once per
+// threshold (c is the middle of the threshold range; used when both factors
+// stay inside the float range, else every pair takes exp2 directly).
+// Sums are float64 per lane and per workgroup (LDS), and workgroups combine in
+// 64-bit fixed point so the result is independent of scheduling.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "ecc_device.hpp"
+#include "ecc_internal.hpp"
+
+namespace ecc {
+namespace {
+
+constexpr int kTileVox = 1024;          // voxels per tile
+constexpr int kTermCap = 4 * kTileVox;  // at most 4 terms per voxel
+constexpr int kChunk = 256;             // thresholds per sweep chunk (4 per lane)
+
+// 2^a for |a| well inside the float range, accurate to ~1 ulp: split off the
+// integer part in float64 so the float exp2 only sees [0, 1).
+__device__ __forceinline__ float exp2_split(double a) {
+  a = fmin(fmax(a, -300.0), 300.0);
+  const double n = floor(a);
+  const float f = (float)(a - n);
+  return ldexpf(exp2f(f), (int)n);
+}
+
+struct Term {
+  float a;  // F = 2^{L (v - c)} (factored) or the value v (direct)
+  float w;  // summed sign
+};
+
+template <bool BWD>
+__global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles, int fx_shift) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  long long* tmp = reinterpret_cast<long long*>(smem);                 // 256
+  int* misc = reinterpret_cast<int*>(tmp + kBlock);                    // [0]=count [1]=flag
+  Term* terms = reinterpret_cast<Term*>(misc + 4);                     // kTermCap
+  double* accS = reinterpret_cast<double*>(terms + kTermCap);          // H
+
+  const int H = p.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* grid = p.grid;
+  const int64_t nz = p.nz, ny = p.ny, nx = p.nx;
+  const int64_t plane = ny * nx, nvox = nz * plane;
+  const float INF = __builtin_inff();
+
+  for (int k = tid; k < H; k += kBlock) accS[k] = 0.0;
+  if (tid == 0) misc[0] = 0;
+
+  // threshold range -> mode and centre
+  float* ftmp = reinterpret_cast<float*>(tmp);
+  {
+    float lo = INF, hi = -INF;
+    for (int k = tid; k < H; k += kBlock) {
+      const float t = p.tau[k];
+      lo = fminf(lo, t);
+      hi = fmaxf(hi, t);
+    }
+    ftmp[tid] = lo;
+    ftmp[kBlock + tid] = hi;
+    __syncthreads();
+    for (int off = kBlock / 2; off > 0; off >>= 1) {
+      if (tid < off) {
+        ftmp[tid] = fminf(ftmp[tid], ftmp[tid + off]);
+        ftmp[kBlock + tid] = fmaxf(ftmp[kBlock + tid], ftmp[kBlock + tid + off]);
+      }
+      __syncthreads();
+    }
+  }
+  const float tlo = ftmp[0], thi = ftmp[kBlock];
+  const double L64 = (double)p.lambda * 1.4426950408889634074;  // lambda * log2(e)
+  const double cen = 0.5 * ((double)tlo + (double)thi);
+  const double half_span = L64 * 0.5 * ((double)thi - (double)tlo);
+  // factored form needs 2^{L(c - tau)} inside [2^-100, 2^100] for every tau
+  const bool factored = (half_span >= 0.0) && (half_span <= 100.0);  // false for inf/NaN spans
+  const float Lf = (float)L64;
+  __syncthreads();
+
+  const int nchunks = (H + kChunk - 1) / kChunk;
+
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    // ---------------- phase A: terms of this tile
+    const int64_t base = t * kTileVox;
+#pragma unroll 1
+    for (int j = 0; j < kTileVox / kBlock; ++j) {
+      const int64_t i = base + j * kBlock + tid;
+      float sv[4] = {INF, INF, INF, INF};
+      int wv[4] = {0, 0, 0, 0};
+      if (i < nvox) {
+        const int64_t x = i % nx;
+        const int64_t yz = i / nx;
+        const int64_t y = yz % ny, z = yz / ny;
+        const bool y1 = y + 1 < ny, z1 = z + 1 < nz;
+        // f[dz][dy][dx+1] for dx in {-1,0,1}
+        float f[2][2][3];
+#pragma unroll
+        for (int dz = 0; dz < 2; ++dz)
+#pragma unroll
+          for (int dy = 0; dy < 2; ++dy)
+#pragma unroll
+            for (int dx = -1; dx <= 1; ++dx) {
+              const bool in = (dz == 0 || z1) && (dy == 0 || y1) && (x + dx >= 0) && (x + dx < nx);
+              f[dz][dy][dx + 1] = in ? grid[i + dz * plane + dy * nx + dx] : INF;
+            }
+        float s[4][3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          s[0][q] = f[0][0][q];
+          s[1][q] = fmaxf(f[0][0][q], f[0][1][q]);
+          s[2][q] = fmaxf(f[0][0][q], f[1][0][q]);
+          s[3][q] = fmaxf(s[1][q], fmaxf(f[1][0][q], f[1][1][q]));
+        }
+        int w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = (int)(s[q][2] > s[q][1]) - (int)(s[q][1] > s[q][0]);
+        w[1] = -w[1];
+        w[2] = -w[2];
+        const float v0 = s[0][1], v1 = s[1][1], v2 = s[2][1], v3 = s[3][1];
+        if (v3 == v2) { w[2] += w[3]; w[3] = 0; }
+        else if (v3 == v1) { w[1] += w[3]; w[3] = 0; }
+        if (v2 == v1) { w[1] += w[2]; w[2] = 0; }
+        if (v1 == v0) { w[0] += w[1]; w[1] = 0; }
+        if (v2 == v0) { w[0] += w[2]; w[2] = 0; }
+        sv[0] = v0; sv[1] = v1; sv[2] = v2; sv[3] = v3;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wv[q] = (sv[q] < INF) ? w[q] : 0;
+      }
+      int cnt = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cnt += (wv[q] != 0);
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      const int total = __shfl(incl, 63);
+      int wbase = 0;
+      if (lane == 63 && total) wbase = atomicAdd(&misc[0], total);
+      wbase = __shfl(wbase, 63);
+      int pos = wbase + incl - cnt;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (wv[q] != 0) {
+          Term tm;
+          // F is kept finite so that F * E overflowing to inf only ever meets a 0 reciprocal
+          tm.a = factored ? fminf(exp2_split(L64 * ((double)sv[q] - cen)), 0x1p126f) : sv[q];
+          tm.w = (float)wv[q];
+          terms[pos++] = tm;
+        }
+      }
+    }
+    __syncthreads();
+    const int n = misc[0];
+
+    // ---------------- phase B: sweep terms x thresholds
+    const int tb = (int)(((int64_t)n * wave) / kWavesPerBlock);
+    const int te = (int)(((int64_t)n * (wave + 1)) / kWavesPerBlock);
+    for (int c = 0; c < nchunks; ++c) {
+      float e[4];
+      bool valid[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int k = c * kChunk + r * 64 + lane;
+        valid[r] = k < H;
+        const float tk = valid[r] ? p.tau[k] : 0.0f;
+        e[r] = factored ? (valid[r] ? exp2_split(L64 * (cen - (double)tk)) : 0.0f) : tk;
+      }
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+      if (factored) {
+        for (int ti = tb; ti < te; ++ti) {
+          const Term tm = terms[ti];
+          const double wd = (double)tm.w;
+          const float wf = tm.w * tm.a;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float d = fmaf(tm.a, e[r], 1.0f);
+            const float rr = __builtin_amdgcn_rcpf(d);
+            if constexpr (!BWD) {
+              acc[r] = fma(wd, (double)rr, acc[r]);
+            } else {
+              const float q = (wf * rr) * (e[r] * rr);  // w t s^2 = w s (1 - s), t = F E
+              acc[r] += (double)q;
+            }
+          }
+        }
+      } else {
+        for (int ti = tb; ti < te; ++ti) {
+          const Term tm = terms[ti];
+          const double wd = (double)tm.w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = fminf(Lf * (tm.a - e[r]), 126.0f);  // L (v - tau), kept finite
+            const float tt = __builtin_amdgcn_exp2f(x);
+            const float rr = __builtin_amdgcn_rcpf(1.0f + tt);
+            if constexpr (!BWD) {
+              acc[r] = fma(wd, (double)rr, acc[r]);
+            } else {
+              const float q = (tm.w * (tt * rr)) * rr;
+              acc[r] += (double)q;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (valid[r]) atomicAdd(&accS[c * kChunk + r * 64 + lane], acc[r]);
+    }
+    __syncthreads();
+    if (tid == 0) misc[0] = 0;
+    __syncthreads();
+  }
+
+  // ---------------- combine workgroups in fixed point
+  unsigned int* ticket = reinterpret_cast<unsigned int*>(p.ws);
+  long long* gacc = reinterpret_cast<long long*>(reinterpret_cast<char*>(p.ws) + kWsHeader);
+  const int stride = acc_bins(H);
+  const double scale = ldexp(1.0, fx_shift);
+  long long* mine = gacc + (size_t)(blockIdx.x % kAccCopies) * stride;
+  __syncthreads();
+  for (int k = tid; k < H; k += kBlock) {
+    const long long q = __double2ll_rn(accS[k] * scale);
+    if (q != 0) agent_add(mine + k, q);
+  }
+  if (!last_block_arrives(ticket, &misc[1])) return;
+  const double inv = ldexp(1.0, -fx_shift);
+  for (int k = tid; k < H; k += kBlock) {
+    long long s = 0;
+#pragma unroll
+    for (int c = 0; c < kAccCopies; ++c) s += agent_load(gacc + (size_t)c * stride + k);
+    double v = (double)s * inv;
+    if constexpr (BWD) v *= (double)p.lambda * (double)p.grad_out[k];
+    p.out[k] = (float)v;
+  }
+  __syncthreads();
+  for (int i = tid; i < kAccCopies * stride; i += kBlock) agent_store(gacc + i, 0LL);
+}
+
+}  // namespace
+
+hipError_t launch_soft(const SoftArgs& a, hipStream_t s) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const int64_t nvox = a.nz * a.ny * a.nx;
+  const int64_t ntiles = (nvox + kTileVox - 1) / kTileVox;
+  int64_t g = (int64_t)di.cus * 4;
+  if (g > ntiles) g = ntiles;
+  if (g < 1) g = 1;
+  // fixed point: |sum| <= #cells <= 8 * nvox per workgroup partial and in total
+  int bits = 0;
+  while (bits < 62 && (((int64_t)1) << bits) < 8 * nvox + 8) ++bits;
+  int shift = 61 - bits;
+  if (shift > 40) shift = 40;
+  const size_t lds = kBlock * sizeof(long long) + 4 * sizeof(int) + kTermCap * sizeof(Term) +
+                     (size_t)a.H * sizeof(double);
+  if (a.grad_out) {
+    auto k = soft_kernel<true>;
+    if (lds > 64 * 1024) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), lds, s, a, ntiles, shift);
+  } else {
+    auto k = soft_kernel<false>;
+    if (lds > 64 * 1024) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), lds, s, a, ntiles, shift);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ecc

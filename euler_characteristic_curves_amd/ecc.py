@@ -1,0 +1,189 @@
+"""Thin PyTorch binding of libecc_mi355 (argument marshalling only).
+
+Every function here takes torch tensors that live on a ROCm device, checks
+their dtype / layout, and calls the C entry point of the same name on the
+current torch stream.  All arithmetic happens in the HIP kernels.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import EccError, check, lib
+
+__all__ = [
+    "ecc_hard_2d", "ecc_hard_3d", "ecc_hard", "ecc_soft_fwd", "ecc_soft_bwd_tau",
+    "workspace_bytes", "get_workspace", "EccError", "SoftECC", "soft_ecc",
+]
+
+_WS = {}
+
+
+def workspace_bytes(op, H, shape=None):
+    n = lib.ecc_workspace_bytes(op, len(shape) if shape else 0, None, int(H))
+    if n == 0:
+        raise EccError(_lib.ECC_E_NTHRESH, f"no workspace size for op={op} H={H}")
+    return int(n)
+
+
+def get_workspace(nbytes, device, stream):
+    """A zero-filled workspace of >= nbytes for this device and stream.
+
+    The library leaves a workspace zero-filled after every call, so one
+    buffer per (device, stream) is reused; calls on one stream never overlap.
+    """
+    key = (device.index, int(stream.cuda_stream))
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        with torch.cuda.stream(stream):
+            ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    return ws
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device)
+
+
+def _grid_dtype(grid):
+    if grid.dtype == torch.uint8:
+        return _lib.ECC_U8
+    if grid.dtype == torch.float32:
+        return _lib.ECC_F32
+    raise TypeError(f"grid dtype {grid.dtype} not supported (uint8 or float32)")
+
+
+def _dev_tensor(t, name, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a ROCm device (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def ecc_hard_2d(grid, tau, out=None, ws=None):
+    """Hard ECC of a 2D uint8/float32 grid: int64[H] (see include/ecc.h)."""
+    _dev_tensor(grid, "grid")
+    if grid.dim() != 2:
+        raise ValueError("grid must be 2D")
+    _dev_tensor(tau, "tau", torch.float32, grid.device)
+    H = tau.numel()
+    if out is None:
+        out = torch.empty(H, dtype=torch.int64, device=grid.device)
+    _dev_tensor(out, "out", torch.int64, grid.device)
+    s = _stream(grid)
+    nb = workspace_bytes(_lib.ECC_OP_HARD, H)
+    ws = get_workspace(nb, grid.device, s) if ws is None else ws
+    check(lib.ecc_hard_2d(_ptr(grid), _grid_dtype(grid), grid.shape[0], grid.shape[1], _ptr(tau), H,
+                          _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                          ctypes.c_void_p(s.cuda_stream)), "ecc_hard_2d")
+    return out
+
+
+def ecc_hard_3d(grid, tau, out=None, ws=None):
+    """Hard ECC of a 3D uint8/float32 grid: int64[H] (see include/ecc.h)."""
+    _dev_tensor(grid, "grid")
+    if grid.dim() != 3:
+        raise ValueError("grid must be 3D")
+    _dev_tensor(tau, "tau", torch.float32, grid.device)
+    H = tau.numel()
+    if out is None:
+        out = torch.empty(H, dtype=torch.int64, device=grid.device)
+    _dev_tensor(out, "out", torch.int64, grid.device)
+    s = _stream(grid)
+    nb = workspace_bytes(_lib.ECC_OP_HARD, H)
+    ws = get_workspace(nb, grid.device, s) if ws is None else ws
+    check(lib.ecc_hard_3d(_ptr(grid), _grid_dtype(grid), grid.shape[0], grid.shape[1], grid.shape[2],
+                          _ptr(tau), H, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                          ctypes.c_void_p(s.cuda_stream)), "ecc_hard_3d")
+    return out
+
+
+def ecc_hard(grid, tau, out=None, ws=None):
+    """Dispatch on grid.dim(): ecc_hard_2d or ecc_hard_3d."""
+    if grid.dim() == 2:
+        return ecc_hard_2d(grid, tau, out, ws)
+    if grid.dim() == 3:
+        return ecc_hard_3d(grid, tau, out, ws)
+    raise ValueError("grid must be 2D or 3D")
+
+
+def _shape_arr(grid):
+    if grid.dim() not in (2, 3):
+        raise ValueError("grid must be 2D or 3D")
+    return (ctypes.c_int64 * grid.dim())(*grid.shape)
+
+
+def ecc_soft_fwd(grid, tau, lam, out=None, ws=None):
+    """Soft ECC forward, float32[H] (see include/ecc.h)."""
+    _dev_tensor(grid, "grid", torch.float32)
+    _dev_tensor(tau, "tau", torch.float32, grid.device)
+    H = tau.numel()
+    if out is None:
+        out = torch.empty(H, dtype=torch.float32, device=grid.device)
+    _dev_tensor(out, "out", torch.float32, grid.device)
+    shp = _shape_arr(grid)
+    s = _stream(grid)
+    nb = workspace_bytes(_lib.ECC_OP_SOFT_FWD, H)
+    ws = get_workspace(nb, grid.device, s) if ws is None else ws
+    check(lib.ecc_soft_fwd(_ptr(grid), grid.dim(), ctypes.cast(shp, ctypes.c_void_p), _ptr(tau), H,
+                           float(lam), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                           ctypes.c_void_p(s.cuda_stream)), "ecc_soft_fwd")
+    return out
+
+
+def ecc_soft_bwd_tau(grid, tau, lam, grad_out, grad_tau=None, ws=None):
+    """dL/dtau of the soft ECC, float32[H] (see include/ecc.h)."""
+    _dev_tensor(grid, "grid", torch.float32)
+    _dev_tensor(tau, "tau", torch.float32, grid.device)
+    _dev_tensor(grad_out, "grad_out", torch.float32, grid.device)
+    H = tau.numel()
+    if grad_out.numel() != H:
+        raise ValueError("grad_out must have H elements")
+    if grad_tau is None:
+        grad_tau = torch.empty(H, dtype=torch.float32, device=grid.device)
+    _dev_tensor(grad_tau, "grad_tau", torch.float32, grid.device)
+    shp = _shape_arr(grid)
+    s = _stream(grid)
+    nb = workspace_bytes(_lib.ECC_OP_SOFT_BWD, H)
+    ws = get_workspace(nb, grid.device, s) if ws is None else ws
+    check(lib.ecc_soft_bwd_tau(_ptr(grid), grid.dim(), ctypes.cast(shp, ctypes.c_void_p), _ptr(tau), H,
+                               float(lam), _ptr(grad_out), _ptr(grad_tau), _ptr(ws),
+                               ws.numel() * ws.element_size(), ctypes.c_void_p(s.cuda_stream)),
+          "ecc_soft_bwd_tau")
+    return grad_tau
+
+
+class SoftECC(torch.autograd.Function):
+    """Autograd wrapper: soft ECC with learnable thresholds (grid gradient not provided)."""
+
+    @staticmethod
+    def forward(ctx, grid, tau, lam):
+        ctx.save_for_backward(grid, tau)
+        ctx.lam = float(lam)
+        return ecc_soft_fwd(grid.detach().contiguous(), tau.detach().contiguous(), lam)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        grid, tau = ctx.saved_tensors
+        if ctx.needs_input_grad[0]:
+            raise NotImplementedError("the gradient with respect to the grid is not implemented")
+        g = ecc_soft_bwd_tau(grid.detach().contiguous(), tau.detach().contiguous(), ctx.lam,
+                             grad_out.contiguous())
+        return None, g, None
+
+
+def soft_ecc(grid, tau, lam):
+    """Soft ECC as an autograd op (differentiable in tau)."""
+    return SoftECC.apply(grid, tau, lam)

@@ -1,0 +1,142 @@
+/*
+ * ecc.h -- C ABI of libecc_mi355.so: Euler characteristic curves of dense 2D/3D
+ * grids on AMD Instinct MI355X (gfx950).
+ *
+ * Method: page "Scalable GPU-Accelerated Euler Characteristic Curves:
+ * Optimization and Differentiable Learning for PyTorch" (paper notes),
+ * section "Method / Key designs":
+ *   - full-sweep kernel: every voxel's local contribution lands in an
+ *     H-bin histogram kept per workgroup, flushed once per bin to global
+ *     memory, and the curve is the running sum of that histogram;
+ *   - local Euler-coefficient computation: chi splits into per-voxel
+ *     contributions that need only a voxel's neighbourhood;
+ *   - differentiable ECC layer: the hard sublevel indicator of
+ *     value <= tau is replaced by a sigmoid of lambda*(tau - value), with an
+ *     analytic backward pass for the thresholds.
+ *
+ * The complex: the grid's voxels are the vertices of a cubical complex.  Voxel
+ * p owns its vertex and the edges, squares and (3D) cube that reach from p
+ * towards +x, +y (, +z) and lie inside the grid.  A cell's value is the max
+ * of its corner values; its sign is (-1)^dim.
+ *
+ * Conventions shared by every entry point:
+ *   - Grids are C-contiguous, x (last index) fastest: grid[ny][nx] or
+ *     grid[nz][ny][nx].  Any base alignment is accepted; 16-byte-aligned
+ *     bases with a row pitch that is a multiple of 16 bytes take the fast
+ *     vector-load path.
+ *   - All pointers except `shape` are DEVICE pointers owned by the caller.
+ *     The library allocates nothing per call and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work and return; outputs are valid once the stream reaches
+ *     that point.  Calls that share one workspace must not overlap in time.
+ *   - Workspace: `ws` must hold ecc_workspace_bytes(...) bytes.  Before its
+ *     FIRST use it must be zero-filled by the caller (e.g. torch.zeros);
+ *     every call leaves it zero-filled again when it completes, so it can be
+ *     reused by the next call on the same stream without clearing.
+ *   - Errors: every entry point returns ECC_OK or an ECC_E_* code.  Argument
+ *     errors are detected on the host before anything is enqueued; a launch
+ *     failure returns ECC_E_HIP.  ecc_last_error() returns a thread-local
+ *     message for the last failing call.  Nothing is printed and no C++
+ *     exception crosses the ABI.
+ *   - Not checked (documented preconditions): grid values are finite (NaN
+ *     is unspecified); buffers are large enough for the shape given.
+ */
+#ifndef ECC_MI355_H
+#define ECC_MI355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define ECC_OK 0
+#define ECC_E_NULL 1      /* a required pointer is NULL                      */
+#define ECC_E_SHAPE 2     /* ndim not 2/3, a dimension < 1, or too many voxels */
+#define ECC_E_DTYPE 3     /* dtype is not ECC_U8 / ECC_F32                    */
+#define ECC_E_NTHRESH 4   /* H < 1 or H > ECC_MAX_THRESHOLDS                  */
+#define ECC_E_LAMBDA 5    /* lambda not finite or <= 0                        */
+#define ECC_E_WORKSPACE 6 /* ws is NULL or ws_bytes is too small              */
+#define ECC_E_HIP 7       /* the HIP runtime reported an error               */
+
+/* grid element types */
+#define ECC_U8 0
+#define ECC_F32 1
+
+/* operations, for ecc_workspace_bytes */
+#define ECC_OP_HARD 0
+#define ECC_OP_SOFT_FWD 1
+#define ECC_OP_SOFT_BWD 2
+
+#define ECC_MAX_THRESHOLDS 8192
+#define ECC_MAX_VOXELS (((int64_t)1) << 40)
+
+/*
+ * Hard ECC of a 2D grid (full-sweep kernel).
+ *   grid    device, dtype elements, [ny][nx]
+ *   tau     device float32[H]: the thresholds
+ *   out     device int64[H]:   out[k] = sum over cells c of (-1)^dim(c) *
+ *           [bin(c) <= k], where bin(c) = min{j : value(c) <= tau_j} with an
+ *           exact IEEE float32 comparison (uint8 values are widened exactly).
+ *           For non-decreasing tau, out[k] is the Euler characteristic of the
+ *           sublevel complex {c : value(c) <= tau_k}; for any other order it
+ *           is that of the running maximum of tau_0..tau_k.
+ *   ws      device workspace, see the conventions above.
+ * One kernel launch.  Result bit-exact (integer arithmetic throughout).
+ */
+int ecc_hard_2d(const void* grid, int dtype, int64_t ny, int64_t nx, const float* tau, int32_t H,
+                int64_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Hard ECC of a 3D grid [nz][ny][nx]; otherwise as ecc_hard_2d. */
+int ecc_hard_3d(const void* grid, int dtype, int64_t nz, int64_t ny, int64_t nx, const float* tau,
+                int32_t H, int64_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Soft ECC forward (differentiable ECC layer).
+ *   grid    device float32, ndim in {2,3}, shape[ndim] (HOST array, slowest first)
+ *   tau     device float32[H]; lambda > 0 and finite (inverse temperature)
+ *   out     device float32[H]: out[k] = sum_c (-1)^dim(c) *
+ *           sigmoid(lambda * (tau_k - value(c))), sigmoid(z) = 1/(1+exp(-z)).
+ * Sigmoids are evaluated in float32, summed in float64 per workgroup and
+ * combined across workgroups in 64-bit fixed point, so the result does not
+ * depend on scheduling.  One kernel launch.
+ */
+int ecc_soft_fwd(const float* grid, int32_t ndim, const int64_t* shape, const float* tau, int32_t H,
+                 float lambda, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Soft ECC backward with respect to the thresholds.
+ *   grad_out  device float32[H]: dL/dout
+ *   grad_tau  device float32[H]: OVERWRITTEN with dL/dtau_k =
+ *             grad_out[k] * lambda * sum_c (-1)^dim(c) s(x)(1 - s(x)),
+ *             x = lambda * (tau_k - value(c)), s = sigmoid.
+ * (out[k] depends on tau_k only, so the Jacobian is diagonal.)  Same
+ * arithmetic and determinism as ecc_soft_fwd.  One kernel launch.
+ */
+int ecc_soft_bwd_tau(const float* grid, int32_t ndim, const int64_t* shape, const float* tau,
+                     int32_t H, float lambda, const float* grad_out, float* grad_tau, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * Bytes of workspace needed by an operation (ECC_OP_*) for a grid of `ndim`
+ * dimensions `shape` (host array; may be NULL, the size does not depend on
+ * it today) and H thresholds.  Returns 0 for invalid op/H.
+ */
+size_t ecc_workspace_bytes(int op, int32_t ndim, const int64_t* shape, int32_t H);
+
+/* Static text for a status code (never NULL). */
+const char* ecc_status_string(int status);
+
+/* Thread-local detail message of the last failing call on this thread ("" if none). */
+const char* ecc_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* ecc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ECC_MI355_H */

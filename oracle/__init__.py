@@ -34,10 +34,13 @@ from .ecc import (  # noqa: F401
     first_k_bins,
     ecc_hard,
     ecc_at,
+    ecc_at_many,
     ecc_soft,
     ecc_soft_percell,
     ecc_soft_at,
+    ecc_soft_at_many,
     ecc_soft_bwd_tau,
     ecc_soft_bwd_at,
+    ecc_soft_bwd_at_many,
     sigmoid,
 )

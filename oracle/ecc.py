@@ -26,7 +26,8 @@ import numpy as np
 __all__ = [
     "cell_values", "cell_counts", "first_k_bins", "ecc_hard", "ecc_at",
     "sigmoid", "ecc_soft", "ecc_soft_percell", "ecc_soft_at",
-    "ecc_soft_bwd_tau", "ecc_soft_bwd_at",
+    "ecc_soft_bwd_tau", "ecc_soft_bwd_at", "ecc_at_many", "ecc_soft_at_many",
+    "ecc_soft_bwd_at_many",
 ]
 
 
@@ -161,6 +162,19 @@ def ecc_at(grid, t, slab=32):
     return chi
 
 
+def ecc_at_many(grid, ts, slab=32):
+    """ecc_at for several thresholds with one pass over the cells (int64 array)."""
+    grid = _check_grid(grid)
+    t = np.asarray(ts, dtype=np.float32).astype(np.float64).ravel()
+    chi = np.zeros(t.size, dtype=np.int64)
+    for sub, keep in _z_slabs(grid, slab):
+        for val, dim in _slab_cells(sub, keep):
+            v = val.astype(np.float64)
+            for i, ti in enumerate(t):
+                chi[i] += (-1) ** dim * int(np.count_nonzero(v <= ti))
+    return chi
+
+
 def sigmoid(x):
     """Logistic function 1/(1+exp(-x)) in float64, evaluated via exp(-|x|)."""
     x = np.asarray(x, dtype=np.float64)
@@ -246,6 +260,33 @@ def ecc_soft_at(grid, t, lam, slab=32):
         for val, dim in _slab_cells(sub, keep):
             acc += (-1) ** dim * float(sigmoid(lam * (t - val.astype(np.float64))).sum())
     return acc
+
+
+def ecc_soft_at_many(grid, ts, lam, slab=32):
+    """ecc_soft_at for several thresholds with one pass over the cells (float64 array)."""
+    t = np.asarray(ts, dtype=np.float32).astype(np.float64).ravel()
+    lam = _check_lambda(lam)
+    acc = np.zeros(t.size, dtype=np.float64)
+    for sub, keep in _z_slabs(_check_grid(grid), slab):
+        for val, dim in _slab_cells(sub, keep):
+            v = val.astype(np.float64)
+            for i, ti in enumerate(t):
+                acc[i] += (-1) ** dim * float(sigmoid(lam * (ti - v)).sum())
+    return acc
+
+
+def ecc_soft_bwd_at_many(grid, ts, lam, gs, slab=32):
+    """ecc_soft_bwd_at for several thresholds with one pass over the cells."""
+    t = np.asarray(ts, dtype=np.float32).astype(np.float64).ravel()
+    g = np.asarray(gs, dtype=np.float32).astype(np.float64).ravel()
+    lam = _check_lambda(lam)
+    acc = np.zeros(t.size, dtype=np.float64)
+    for sub, keep in _z_slabs(_check_grid(grid), slab):
+        for val, dim in _slab_cells(sub, keep):
+            v = val.astype(np.float64)
+            for i, ti in enumerate(t):
+                acc[i] += (-1) ** dim * float(_dsig(lam * (ti - v)).sum())
+    return g * lam * acc
 
 
 def ecc_soft_bwd_tau(grid, tau, lam, grad_out, slab=32):
