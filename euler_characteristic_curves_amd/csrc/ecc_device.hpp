@@ -15,27 +15,57 @@ __device__ __forceinline__ long long agent_load(const long long* p) {
 __device__ __forceinline__ void agent_store(long long* p, long long v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void agent_add(long long* p, long long v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+__device__ __forceinline__ double agent_load(const double* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void agent_store(double* p, double v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Completion ticket: every workgroup calls this once after its global
-// atomics; exactly one (the last to arrive) gets true.  The ticket is reset
-// to zero by that workgroup so the workspace is clean for the next call.
-__device__ __forceinline__ bool last_block_arrives(unsigned int* ticket, int* lds_flag) {
-  __threadfence();
-  __syncthreads();
+// Grid-wide reduction of per-workgroup rows of n int64 values, one launch.
+//
+// Every workgroup adds its non-zero values into one of kAccCopies int64
+// accumulator rows with device-scope atomic adds, waits until all of its own
+// memory operations are acknowledged, and only then takes a ticket.  On this
+// GPU, device-scope atomics are performed at the point of coherence shared by
+// all XCDs and a wave's vmcnt reaches zero only once they are, so a workgroup
+// that draws the last ticket can read every other workgroup's contribution
+// with device-scope atomic loads.  This replaces agent-scope fences, which
+// write back and invalidate the issuing XCD's L2 and cost far more than the
+// reduction itself when every workgroup issues them.  The last workgroup
+// returns true with the totals in `tot` (LDS, n entries) and leaves the
+// accumulators and the ticket zero for the next launch.  Integer addition is
+// associative, so the totals do not depend on the order of arrival.
+template <typename Local>
+__device__ bool grid_reduce(void* ws, int H, int n, Local local, long long* tot, int* lds_flag) {
+  unsigned int* ticket = reinterpret_cast<unsigned int*>(ws);
+  long long* acc = reinterpret_cast<long long*>(reinterpret_cast<char*>(ws) + kWsHeader);
+  const int stride = acc_bins(H);
+  long long* mine = acc + (size_t)(blockIdx.x % kAccCopies) * stride;
+  for (int b = threadIdx.x; b < n; b += kBlock) {
+    const long long v = local(b);
+    if (v != 0) __hip_atomic_fetch_add(mine + b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's atomics are acknowledged
+  __syncthreads();                // ... and every other wave's of this workgroup
   if (threadIdx.x == 0) {
-    unsigned int prev =
-        __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    int last = (prev == gridDim.x - 1);
+    const unsigned int prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (prev == gridDim.x - 1);
     if (last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *lds_flag = last;
   }
   __syncthreads();
-  bool last = *lds_flag != 0;
-  if (last) __threadfence();
-  return last;
+  if (!*lds_flag) return false;
+  for (int b = threadIdx.x; b < n; b += kBlock) {
+    long long s = 0;
+#pragma unroll
+    for (int c = 0; c < kAccCopies; ++c) s += agent_load(acc + (size_t)c * stride + b);
+    tot[b] = s;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kAccCopies * stride; i += kBlock) agent_store(acc + i, 0LL);
+  return true;
 }
 
 // --------------------------------------------------------- block scans

@@ -47,13 +47,18 @@ struct BinCtx {
   int trash;       // key of "no threshold admits this cell"
 };
 
+// Exact bin of one float (slow path: edge tiles and unaligned grids), out of line.
+__device__ __attribute__((noinline)) int bin_generic(float v, const float* R, int H, float r0, float scale) {
+  return bin_of(v, R, H, r0, scale);
+}
+
 template <int DT>
 __device__ __forceinline__ int key_of(typename Elem<DT>::T v, const BinCtx& c) {
   if constexpr (DT == 0) {
     (void)c;
     return (int)v;
   } else {
-    return bin_of(v, c.R, c.H, c.r0, c.scale);
+    return bin_generic(v, c.R, c.H, c.r0, c.scale);
   }
 }
 
@@ -110,39 +115,87 @@ __device__ __forceinline__ int tele(int prev, int cur, int next) {
   return (int)(next > cur) - (int)(cur > prev);
 }
 
-// ------------------------------------------------------------ shared tail
-// Flush the workgroup histogram with one global atomic per non-zero bin, then
-// let the last workgroup build the curve and re-zero the workspace.
-template <int DT, int C>
-__device__ void flush_and_finish(const HardArgs& a, int nbins, int* hist, long long* tmp,
-                                 long long* ch, int* flag) {
-  unsigned int* ticket = reinterpret_cast<unsigned int*>(a.ws);
-  long long* acc = reinterpret_cast<long long*>(reinterpret_cast<char*>(a.ws) + kWsHeader);
-  const int stride = acc_bins(a.H);
-  __syncthreads();
-  long long* mine = acc + (size_t)(blockIdx.x % kAccCopies) * stride;
-  for (int b = threadIdx.x; b < nbins; b += kBlock) {
-    int s = 0;
-#pragma unroll
-    for (int c = 0; c < C; ++c) s += hist[b * C + c];
-    if (s != 0) agent_add(mine + b, (long long)s);
-  }
-  if (!last_block_arrives(ticket, flag)) return;
+// ------------------------------------------------------- fast-path helpers
+// Cross-lane neighbours with DPP wave shifts (no LDS traffic).  Lane i gets
+// lane i-1's (from_left) / lane i+1's (from_right) value; the lane at the end
+// of the wave, which has no source lane, gets `edge`.
+__device__ __forceinline__ int from_left(int v, int edge) {
+  return __builtin_amdgcn_update_dpp(edge, v, 0x138 /* wave_shr:1 */, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int from_right(int v, int edge) {
+  return __builtin_amdgcn_update_dpp(edge, v, 0x130 /* wave_shl:1 */, 0xF, 0xF, false);
+}
 
-  auto total = [&](int i) {
+// Telescoped weights of one row sequence over this lane's V positions and
+// unconditional histogram updates (an update of 0 costs the same LDS time as
+// a masked one, and needs no exec-mask branches).  sign is +1 or -1.
+template <int V, int C>
+__device__ __forceinline__ void tele_add(const int (&s)[V], int left, int right, int sign, int* hist,
+                                         int lofs) {
+  int inc_prev = (int)(s[0] > left);
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int nxt = j + 1 < V ? s[j + 1] : right;
+    const int inc = (int)(nxt > s[j]);
+    const int w = inc - inc_prev;
+    inc_prev = inc;
+    atomicAdd(&hist[s[j] * C + lofs], sign > 0 ? w : -w);
+  }
+}
+
+// Binning table for float grids: P[k] = (R[k-1], R[k]) with R[-1] = -inf and
+// R[H] = +inf, so v belongs to bin k iff P[k].x < v <= P[k].y.
+__device__ __forceinline__ void build_pairs(const float* R, int H, float2* P) {
+  for (int k = threadIdx.x; k <= H; k += kBlock)
+    P[k] = make_float2(k > 0 ? R[k - 1] : -__builtin_inff(), k < H ? R[k] : __builtin_inff());
+}
+
+// First k with v <= R[k] (or H) by binary search: the rare fallback of bin_fast,
+// kept out of line so the unrolled fast path stays small.
+__device__ __attribute__((noinline)) int bin_search(float v, const float* R, int H) {
+  int lo = 0, hi = H;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (v <= R[mid]) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+// One LDS read per voxel when the linear guess lands in the right bin; exact
+// fallback (binary search on R) otherwise.
+__device__ __forceinline__ int bin_fast(float v, const float2* P, const float* R, int H, float mul,
+                                        float add) {
+  float g = ceilf(fmaf(v, mul, add));
+  g = fminf(fmaxf(g, 0.0f), (float)H);  // NaN -> 0
+  int k = (int)g;
+  const float2 p = P[k];
+  if (!(p.x < v && v <= p.y)) k = bin_search(v, R, H);
+  return k;
+}
+
+// ------------------------------------------------------------ shared tail
+// Reduce the workgroup histograms over the grid and let the last workgroup
+// turn the totals into the curve.  `tot`
+// is LDS for nbins int64 that may alias the (no longer needed) histogram.
+template <int DT, int C>
+__device__ __forceinline__ void flush_and_finish(const HardArgs& a, int nbins, int* hist, long long* tmp,
+                                                 long long* ch, int* flag, long long* tot) {
+  __syncthreads();
+  auto local = [&](int b) {
     long long s = 0;
 #pragma unroll
-    for (int c = 0; c < kAccCopies; ++c) s += agent_load(acc + (size_t)c * stride + i);
+    for (int c = 0; c < C; ++c) s += hist[b * C + c];
     return s;
   };
+  if (!grid_reduce(a.ws, a.H, nbins, local, tot, flag)) return;
+  int64_t* out = a.out;
   if constexpr (DT == 0) {
-    // per-value histogram -> cumulative count of values <= v
+    // per-value histogram -> weighted count of values <= v
     block_scan<long long>(
-        256, 0LL, [](long long x, long long y) { return x + y; }, total,
+        256, 0LL, [](long long x, long long y) { return x + y; }, [&](int i) { return tot[i]; },
         [&](int i, long long v) { ch[i] = v; }, tmp);
-    // out[k] = #(values <= R_k) weighted, R = running max of tau
+    // out[k] = weighted count of values <= R_k, R = running max of tau
     float* ftmp = reinterpret_cast<float*>(tmp);
-    int64_t* out = a.out;
     block_scan<float>(
         a.H, -__builtin_inff(), [](float x, float y) { return fmaxf(x, y); },
         [&](int i) { return a.tau[i]; },
@@ -154,12 +207,10 @@ __device__ void flush_and_finish(const HardArgs& a, int nbins, int* hist, long l
         },
         ftmp);
   } else {
-    int64_t* out = a.out;
     block_scan<long long>(
-        a.H, 0LL, [](long long x, long long y) { return x + y; }, total,
+        a.H, 0LL, [](long long x, long long y) { return x + y; }, [&](int i) { return tot[i]; },
         [&](int i, long long v) { out[i] = v; }, tmp);
   }
-  for (int i = threadIdx.x; i < kAccCopies * stride; i += kBlock) agent_store(acc + i, 0LL);
 }
 
 template <int DT>
@@ -176,30 +227,245 @@ __device__ __forceinline__ void setup_bins(const HardArgs& a, float* R, long lon
   }
 }
 
+// ------------------------------------------------------------ raw rows
+// One row slice of a wave: VEC elements per lane plus the two elements just
+// outside the wave's column chunk (needed by lanes 0 and 63).
+template <int DT, int VEC> struct RawRow;
+template <> struct RawRow<0, 16> { uint4 v; uint8_t l, r; };
+template <> struct RawRow<0, 8> { uint2 v; uint8_t l, r; };
+template <> struct RawRow<1, 4> { float4 v; float l, r; };
+
+// Loads are unconditional: callers clamp the row pointer to a valid row and
+// the edge columns to valid columns, and apply validity when forming keys, so
+// the compiler can keep several loads in flight across loop iterations.
+template <int DT, int VEC>
+__device__ __forceinline__ void fetch_row(RawRow<DT, VEC>& raw, const typename Elem<DT>::T* row,
+                                          int64_t xb, int lane, int64_t xl, int64_t xr) {
+  if constexpr (DT == 0 && VEC == 16) raw.v = *reinterpret_cast<const uint4*>(row + xb + lane * VEC);
+  if constexpr (DT == 0 && VEC == 8) raw.v = *reinterpret_cast<const uint2*>(row + xb + lane * VEC);
+  if constexpr (DT == 1) raw.v = *reinterpret_cast<const float4*>(row + xb + lane * VEC);
+  raw.l = row[xl];
+  raw.r = row[xr];
+}
+
+struct FastBin {
+  const float2* P;
+  const float* R;
+  int H;
+  float mul, add;
+};
+
+template <int DT>
+__device__ __forceinline__ int fkey(typename Elem<DT>::T v, const FastBin& fb) {
+  if constexpr (DT == 0) {
+    (void)fb;
+    return (int)v;
+  } else {
+    return bin_fast(v, fb.P, fb.R, fb.H, fb.mul, fb.add);
+  }
+}
+
+// Keys of a fetched row.  The loaded registers are always consumed (validity
+// is applied afterwards with selects), so no load is left pending on any
+// path.  CHECK=false skips the selects for rows known to be inside the grid.
+template <int DT, int VEC, bool CHECK = true>
+__device__ __forceinline__ void row_keys(const RawRow<DT, VEC>& raw, bool valid, bool has_l, bool has_r,
+                                         int trash, const FastBin& fb, int (&k)[VEC], int& kl, int& kr) {
+  if constexpr (DT == 0) {
+    unsigned int w[VEC / 4];
+    if constexpr (VEC == 16) { w[0] = raw.v.x; w[1] = raw.v.y; w[2] = raw.v.z; w[3] = raw.v.w; }
+    else { w[0] = raw.v.x; w[1] = raw.v.y; }
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) k[j] = (int)((w[j >> 2] >> (8 * (j & 3))) & 0xffu);
+  } else {
+    k[0] = fkey<DT>(raw.v.x, fb);
+    k[1] = fkey<DT>(raw.v.y, fb);
+    k[2] = fkey<DT>(raw.v.z, fb);
+    k[3] = fkey<DT>(raw.v.w, fb);
+  }
+  kl = fkey<DT>(raw.l, fb);
+  kr = fkey<DT>(raw.r, fb);
+  if constexpr (CHECK) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) k[j] = valid ? k[j] : trash;
+  }
+  kl = (valid && has_l) ? kl : trash;
+  kr = (valid && has_r) ? kr : trash;
+}
+
 // ------------------------------------------------------------------- 2D
-// Workgroup tile: 4 waves stacked in y, each wave owns TH rows of a chunk of
-// 64*VEC columns and marches down them, keeping the current row's keys in
-// registers and loading the next.
+// Interior wave tile: the column chunk lies inside the grid and rows are
+// 16-byte aligned.  Rows ys..ye-1 are processed (row ye is the halo), with
+// two rows of loads in flight ahead of the row being processed.
+// One row step: cur/nxt keys of rows y and y+1 (lane-local), edge keys from
+// outside the chunk; two telescoped sequences (the row and the max of the two
+// rows) go to the histogram.
+template <int VEC, int C>
+__device__ __forceinline__ void row2d(const int (&cur)[VEC], int cl, int cr, const int (&nxt)[VEC], int nl,
+                                      int nr, int* hist, int lofs) {
+  int s2[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) s2[j] = max(cur[j], nxt[j]);
+  tele_add<VEC, C>(cur, from_left(cur[VEC - 1], cl), from_right(cur[0], cr), 1, hist, lofs);
+  tele_add<VEC, C>(s2, from_left(s2[VEC - 1], max(cl, nl)), from_right(s2[0], max(cr, nr)), -1, hist,
+                   lofs);
+}
+
+// Interior wave tile (aligned rows, column chunk inside the grid).  Rows
+// ys..ye-1 are processed, row ye is the halo.  Four rows of loads are in
+// flight: the row loop is unrolled by 4 so every load lands in a register
+// that is consumed in place (a register copy of an in-flight load would force
+// the wave to wait for it).  Rows past the grid are loaded from the last row
+// (always a valid address) and turned into trash keys.
+template <int DT, int VEC, int C>
+__device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, int64_t ny, int64_t nx,
+                                            int64_t ys, int64_t ye, int64_t xb, int lane, int lofs,
+                                            int* hist, int trash, const FastBin& fb) {
+  using T = typename Elem<DT>::T;
+  constexpr int64_t CHUNK = 64 * VEC;
+  const bool has_l = xb > 0, has_r = xb + CHUNK < nx;
+  const int64_t xl = has_l ? xb - 1 : xb, xr = has_r ? xb + CHUNK : xb;
+  const T* lastrow = grid + (ny - 1) * nx;
+  auto rowp = [&](int64_t y) { return y < ny ? grid + y * nx : lastrow; };
+  RawRow<DT, VEC> q0, q1, q2, q3;
+  int cur[VEC], cl, cr;
+  {
+    RawRow<DT, VEC> r0;
+    fetch_row<DT, VEC>(r0, rowp(ys), xb, lane, xl, xr);
+    fetch_row<DT, VEC>(q0, rowp(ys + 1), xb, lane, xl, xr);
+    fetch_row<DT, VEC>(q1, rowp(ys + 2), xb, lane, xl, xr);
+    fetch_row<DT, VEC>(q2, rowp(ys + 3), xb, lane, xl, xr);
+    fetch_row<DT, VEC>(q3, rowp(ys + 4), xb, lane, xl, xr);
+    row_keys<DT, VEC>(r0, true, has_l, has_r, trash, fb, cur, cl, cr);
+  }
+  int nxt[VEC], nl, nr;
+  // main loop: four rows per trip, every "next" row inside the grid, one load per
+  // stage issued four rows ahead
+#define ECC_ROW2D_FAST(Q, K)                                                         \
+  {                                                                                  \
+    row_keys<DT, VEC, false>(Q, true, has_l, has_r, trash, fb, nxt, nl, nr);         \
+    fetch_row<DT, VEC>(Q, rowp(y + K + 5), xb, lane, xl, xr);                        \
+    row2d<VEC, C>(cur, cl, cr, nxt, nl, nr, hist, lofs);                             \
+    _Pragma("unroll") for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];                 \
+    cl = nl;                                                                         \
+    cr = nr;                                                                         \
+  }
+  // remainder: at most four rows, checked against the tile and grid ends
+#define ECC_ROW2D_TAIL(Q, K)                                                         \
+  if (y + K < ye) {                                                                  \
+    row_keys<DT, VEC, true>(Q, y + K + 1 < ny, has_l, has_r, trash, fb, nxt, nl, nr); \
+    row2d<VEC, C>(cur, cl, cr, nxt, nl, nr, hist, lofs);                             \
+    _Pragma("unroll") for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];                 \
+    cl = nl;                                                                         \
+    cr = nr;                                                                         \
+  }
+  int64_t y = ys;
+  for (; y + 4 <= ye && y + 4 < ny; y += 4) {
+    ECC_ROW2D_FAST(q0, 0)
+    ECC_ROW2D_FAST(q1, 1)
+    ECC_ROW2D_FAST(q2, 2)
+    ECC_ROW2D_FAST(q3, 3)
+  }
+  ECC_ROW2D_TAIL(q0, 0)
+  ECC_ROW2D_TAIL(q1, 1)
+  ECC_ROW2D_TAIL(q2, 2)
+  ECC_ROW2D_TAIL(q3, 3)
+#undef ECC_ROW2D_FAST
+#undef ECC_ROW2D_TAIL
+}
+
+// Any wave tile (edges, unaligned rows): element loads with bounds checks.
+template <int DT, int VEC, int C>
+__device__ __forceinline__ void tile2d_generic(const typename Elem<DT>::T* grid, int64_t ny, int64_t nx,
+                                               int64_t ys, int64_t ye, int64_t xb, int lane, int lofs,
+                                               int* hist, bool vok, const BinCtx& bc) {
+  using T = typename Elem<DT>::T;
+  constexpr int64_t CHUNK = 64 * VEC;
+  const int64_t x0 = xb + lane * VEC;
+  int cur[VEC], nxt[VEC];
+  const T* row = grid + ys * nx;
+  load_keys<DT, VEC>(row, x0, nx, vok, bc, cur);
+  int curL = load_key1<DT>(row, xb - 1, nx, bc);
+  int curR = load_key1<DT>(row, xb + CHUNK, nx, bc);
+  for (int64_t y = ys; y < ye; ++y) {
+    const T* nrow = (y + 1 < ny) ? grid + (y + 1) * nx : nullptr;
+    load_keys<DT, VEC>(nrow, x0, nx, vok, bc, nxt);
+    const int nxtL = load_key1<DT>(nrow, xb - 1, nx, bc);
+    const int nxtR = load_key1<DT>(nrow, xb + CHUNK, nx, bc);
+    int s2[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) s2[j] = max(cur[j], nxt[j]);
+    tele_add<VEC, C>(cur, from_left(cur[VEC - 1], curL), from_right(cur[0], curR), 1, hist, lofs);
+    tele_add<VEC, C>(s2, from_left(s2[VEC - 1], max(curL, nxtL)), from_right(s2[0], max(curR, nxtR)), -1,
+                     hist, lofs);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];
+    curL = nxtL;
+    curR = nxtR;
+  }
+}
+
+struct Lds {
+  long long* tmp;
+  long long* ch;
+  int* flag;
+  int* hist;
+  float* R;
+  float2* P;
+};
+
+__host__ __device__ inline size_t align16(size_t b) { return (b + 15) & ~(size_t)15; }
+
+__host__ __device__ inline size_t lds_layout(int DT, int nbins, int C, int H, size_t* off_hist,
+                                             size_t* off_R, size_t* off_P) {
+  size_t b = 2 * kBlock * sizeof(long long) + 4 * sizeof(int);
+  *off_hist = b;
+  b = align16(b + (size_t)(nbins + 1) * C * sizeof(int));
+  *off_R = b;
+  if (DT == 1) b = align16(b + (size_t)H * sizeof(float));
+  *off_P = b;
+  if (DT == 1) b += (size_t)(H + 1) * sizeof(float2);
+  return b;
+}
+
+template <int DT, int C>
+__device__ __forceinline__ Lds setup_lds(unsigned char* smem, const HardArgs& a, int nbins, BinCtx& bc,
+                                         FastBin& fb) {
+  size_t oh, oR, oP;
+  lds_layout(DT, nbins, C, a.H, &oh, &oR, &oP);
+  Lds L;
+  L.tmp = reinterpret_cast<long long*>(smem);
+  L.ch = L.tmp + kBlock;
+  L.flag = reinterpret_cast<int*>(L.ch + kBlock);
+  L.hist = reinterpret_cast<int*>(smem + oh);
+  L.R = reinterpret_cast<float*>(smem + oR);
+  L.P = reinterpret_cast<float2*>(smem + oP);
+  for (int i = threadIdx.x; i < (nbins + 1) * C; i += kBlock) L.hist[i] = 0;
+  setup_bins<DT>(a, L.R, L.tmp, bc, nbins);
+  fb.P = L.P;
+  fb.R = L.R;
+  fb.H = a.H;
+  fb.mul = bc.scale;
+  fb.add = -bc.r0 * bc.scale;
+  if (!(fb.add > -__builtin_inff() && fb.add < __builtin_inff())) { fb.mul = 0.0f; fb.add = 0.0f; }
+  if constexpr (DT == 1) build_pairs(L.R, a.H, L.P);
+  __syncthreads();
+  return L;
+}
+
 template <int DT, int VEC, int C, int TH>
 __global__ __launch_bounds__(kBlock) void hard2d_kernel(HardArgs a, int nbins, int64_t ntx,
                                                         int64_t ntiles, int vec_ok) {
   extern __shared__ __align__(16) unsigned char smem[];
   using T = typename Elem<DT>::T;
-  long long* tmp = reinterpret_cast<long long*>(smem);            // 256
-  long long* ch = tmp + kBlock;                                    // 256
-  int* flag = reinterpret_cast<int*>(ch + kBlock);                 // 4 ints
-  int* hist = flag + 4;                                            // (nbins+1)*C
-  float* R = reinterpret_cast<float*>(hist + (nbins + 1) * C);     // H (f32)
-
-  for (int i = threadIdx.x; i < (nbins + 1) * C; i += kBlock) hist[i] = 0;
   BinCtx bc;
-  setup_bins<DT>(a, R, tmp, bc, nbins);
-  __syncthreads();
+  FastBin fb;
+  Lds L = setup_lds<DT, C>(smem, a, nbins, bc, fb);
 
   const T* grid = reinterpret_cast<const T*>(a.grid);
   const int64_t ny = a.ny, nx = a.nx;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lofs = lane & (C - 1);
   constexpr int64_t CHUNK = 64 * VEC;
   const bool vok = vec_ok != 0;
@@ -209,75 +475,144 @@ __global__ __launch_bounds__(kBlock) void hard2d_kernel(HardArgs a, int nbins, i
     const int64_t ys = (tyb * kWavesPerBlock + wave) * TH;
     if (ys >= ny) continue;
     const int64_t ye = ys + TH < ny ? ys + TH : ny;
-    const int64_t xb = tx * CHUNK, x0 = xb + lane * VEC;
-
-    int cur[VEC], nxt[VEC];
-    const T* row = grid + ys * nx;
-    load_keys<DT, VEC>(row, x0, nx, vok, bc, cur);
-    int curL = load_key1<DT>(row, xb - 1, nx, bc);
-    int curR = load_key1<DT>(row, xb + CHUNK, nx, bc);
-
-    for (int64_t y = ys; y < ye; ++y) {
-      const T* nrow = (y + 1 < ny) ? grid + (y + 1) * nx : nullptr;
-      load_keys<DT, VEC>(nrow, x0, nx, vok, bc, nxt);
-      const int nxtL = load_key1<DT>(nrow, xb - 1, nx, bc);
-      const int nxtR = load_key1<DT>(nrow, xb + CHUNK, nx, bc);
-
-      int s1[VEC], s2[VEC];
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        s1[j] = cur[j];
-        s2[j] = max(cur[j], nxt[j]);
-      }
-      int s1l = __shfl_up(s1[VEC - 1], 1), s2l = __shfl_up(s2[VEC - 1], 1);
-      int s1r = __shfl_down(s1[0], 1), s2r = __shfl_down(s2[0], 1);
-      if (lane == 0) { s1l = curL; s2l = max(curL, nxtL); }
-      if (lane == 63) { s1r = curR; s2r = max(curR, nxtR); }
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        const int p1 = j ? s1[j - 1] : s1l, n1 = j + 1 < VEC ? s1[j + 1] : s1r;
-        const int p2 = j ? s2[j - 1] : s2l, n2 = j + 1 < VEC ? s2[j + 1] : s2r;
-        int w1 = tele(p1, s1[j], n1);
-        int w2 = -tele(p2, s2[j], n2);
-        if (s1[j] == s2[j]) { w1 += w2; w2 = 0; }
-        if (w1) atomicAdd(&hist[s1[j] * C + lofs], w1);
-        if (w2) atomicAdd(&hist[s2[j] * C + lofs], w2);
-      }
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];
-      curL = nxtL;
-      curR = nxtR;
-    }
+    const int64_t xb = tx * CHUNK;
+    if (vok && xb + CHUNK <= nx)
+      tile2d_fast<DT, VEC, C>(grid, ny, nx, ys, ye, xb, lane, lofs, L.hist, nbins, fb);
+    else
+      tile2d_generic<DT, VEC, C>(grid, ny, nx, ys, ye, xb, lane, lofs, L.hist, vok, bc);
   }
-  flush_and_finish<DT, C>(a, nbins, hist, tmp, ch, flag);
+  long long* tot = C >= 2 ? reinterpret_cast<long long*>(L.hist) : reinterpret_cast<long long*>(L.R);
+  flush_and_finish<DT, C>(a, nbins, L.hist, L.tmp, L.ch, L.flag, tot);
 }
 
 // ------------------------------------------------------------------- 3D
-// Wave tile: a chunk of 64*VEC columns x TY rows x TZ planes.  The wave
-// marches along z holding TY+1 rows (TY plus a one-row halo) of planes z and
-// z+1 in registers; each step loads the TY+1 rows of the next plane.
+// Wave tile: a chunk of 64*VEC columns x TY rows x a range of planes.  The
+// wave marches along z holding the keys of TY+1 rows (TY plus a one-row
+// halo) of planes z and z+1; the raw rows of plane z+2 are in flight while
+// plane z is processed.
+template <int DT, int VEC, int C, int TY>
+__device__ __forceinline__ void rows3d(int (&A)[TY + 1][VEC], int (&AL)[TY + 1], int (&AR)[TY + 1],
+                                       int (&B)[TY + 1][VEC], int (&BL)[TY + 1], int (&BR)[TY + 1],
+                                       int64_t ys, int64_t ny, int* hist, int lofs) {
+#pragma unroll
+  for (int r = 0; r < TY; ++r) {
+    if (ys + r < ny) {
+      int s2[VEC], s3[VEC], s4[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        s2[j] = max(A[r][j], A[r + 1][j]);
+        s3[j] = max(A[r][j], B[r][j]);
+        s4[j] = max(s2[j], max(B[r][j], B[r + 1][j]));
+      }
+      const int e2l = max(AL[r], AL[r + 1]), e3l = max(AL[r], BL[r]), e4l = max(e2l, max(BL[r], BL[r + 1]));
+      const int e2r = max(AR[r], AR[r + 1]), e3r = max(AR[r], BR[r]), e4r = max(e2r, max(BR[r], BR[r + 1]));
+      tele_add<VEC, C>(A[r], from_left(A[r][VEC - 1], AL[r]), from_right(A[r][0], AR[r]), 1, hist, lofs);
+      tele_add<VEC, C>(s2, from_left(s2[VEC - 1], e2l), from_right(s2[0], e2r), -1, hist, lofs);
+      tele_add<VEC, C>(s3, from_left(s3[VEC - 1], e3l), from_right(s3[0], e3r), -1, hist, lofs);
+      tele_add<VEC, C>(s4, from_left(s4[VEC - 1], e4l), from_right(s4[0], e4r), 1, hist, lofs);
+    }
+  }
+}
+
+template <int DT, int VEC, int C, int TY>
+__device__ __forceinline__ void tile3d_fast(const typename Elem<DT>::T* grid, int64_t nz, int64_t ny,
+                                            int64_t nx, int64_t zs, int64_t ze, int64_t ys, int64_t xb,
+                                            int lane, int lofs, int* hist, int trash, const FastBin& fb) {
+  constexpr int64_t CHUNK = 64 * VEC;
+  const int64_t plane = ny * nx;
+  const bool has_l = xb > 0, has_r = xb + CHUNK < nx;
+  const int64_t xl = has_l ? xb - 1 : xb, xr = has_r ? xb + CHUNK : xb;
+  using T = typename Elem<DT>::T;
+  int64_t roff[TY + 1];
+#pragma unroll
+  for (int r = 0; r <= TY; ++r) roff[r] = (ys + r < ny ? ys + r : ny - 1) * nx;
+  auto rowp = [&](int64_t z, int r) -> const T* {
+    return grid + (z < nz ? z : nz - 1) * plane + roff[r];
+  };
+  RawRow<DT, VEC> raw[TY + 1];
+  int A[TY + 1][VEC], AL[TY + 1], AR[TY + 1], B[TY + 1][VEC], BL[TY + 1], BR[TY + 1];
+#pragma unroll
+  for (int r = 0; r <= TY; ++r) fetch_row<DT, VEC>(raw[r], rowp(zs, r), xb, lane, xl, xr);
+#pragma unroll
+  for (int r = 0; r <= TY; ++r) row_keys<DT, VEC>(raw[r], ys + r < ny, has_l, has_r, trash, fb, A[r], AL[r], AR[r]);
+#pragma unroll
+  for (int r = 0; r <= TY; ++r) fetch_row<DT, VEC>(raw[r], rowp(zs + 1, r), xb, lane, xl, xr);
+  const bool rows_in = ys + TY < ny;
+  for (int64_t z = zs; z < ze; ++z) {
+    const bool zn = z + 1 < nz;
+    if (zn && rows_in) {
+#pragma unroll
+      for (int r = 0; r <= TY; ++r)
+        row_keys<DT, VEC, false>(raw[r], true, has_l, has_r, trash, fb, B[r], BL[r], BR[r]);
+    } else {
+#pragma unroll
+      for (int r = 0; r <= TY; ++r)
+        row_keys<DT, VEC, true>(raw[r], zn && ys + r < ny, has_l, has_r, trash, fb, B[r], BL[r], BR[r]);
+    }
+#pragma unroll
+    for (int r = 0; r <= TY; ++r) fetch_row<DT, VEC>(raw[r], rowp(z + 2, r), xb, lane, xl, xr);
+    rows3d<DT, VEC, C, TY>(A, AL, AR, B, BL, BR, ys, ny, hist, lofs);
+#pragma unroll
+    for (int r = 0; r <= TY; ++r) {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) A[r][j] = B[r][j];
+      AL[r] = BL[r];
+      AR[r] = BR[r];
+    }
+  }
+}
+
+template <int DT, int VEC, int C, int TY>
+__device__ __forceinline__ void tile3d_generic(const typename Elem<DT>::T* grid, int64_t nz, int64_t ny,
+                                               int64_t nx, int64_t zs, int64_t ze, int64_t ys, int64_t xb,
+                                               int lofs, int* hist, bool vok, const BinCtx& bc, int lane) {
+  using T = typename Elem<DT>::T;
+  constexpr int64_t CHUNK = 64 * VEC;
+  const int64_t plane = ny * nx;
+  const int64_t x0 = xb + lane * VEC;
+  int A[TY + 1][VEC], B[TY + 1][VEC];
+  int AL[TY + 1], AR[TY + 1], BL[TY + 1], BR[TY + 1];
+#pragma unroll
+  for (int r = 0; r <= TY; ++r) {
+    const T* row = (ys + r < ny) ? grid + zs * plane + (ys + r) * nx : nullptr;
+    load_keys<DT, VEC>(row, x0, nx, vok, bc, A[r]);
+    AL[r] = load_key1<DT>(row, xb - 1, nx, bc);
+    AR[r] = load_key1<DT>(row, xb + CHUNK, nx, bc);
+  }
+  for (int64_t z = zs; z < ze; ++z) {
+    const bool zn = z + 1 < nz;
+#pragma unroll
+    for (int r = 0; r <= TY; ++r) {
+      const T* row = (zn && ys + r < ny) ? grid + (z + 1) * plane + (ys + r) * nx : nullptr;
+      load_keys<DT, VEC>(row, x0, nx, vok, bc, B[r]);
+      BL[r] = load_key1<DT>(row, xb - 1, nx, bc);
+      BR[r] = load_key1<DT>(row, xb + CHUNK, nx, bc);
+    }
+    rows3d<DT, VEC, C, TY>(A, AL, AR, B, BL, BR, ys, ny, hist, lofs);
+#pragma unroll
+    for (int r = 0; r <= TY; ++r) {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) A[r][j] = B[r][j];
+      AL[r] = BL[r];
+      AR[r] = BR[r];
+    }
+  }
+}
+
 template <int DT, int VEC, int C, int TY>
 __global__ __launch_bounds__(kBlock) void hard3d_kernel(HardArgs a, int nbins, int64_t ntx,
                                                         int64_t nty4, int64_t TZ, int64_t ntiles,
                                                         int vec_ok) {
   extern __shared__ __align__(16) unsigned char smem[];
   using T = typename Elem<DT>::T;
-  long long* tmp = reinterpret_cast<long long*>(smem);
-  long long* ch = tmp + kBlock;
-  int* flag = reinterpret_cast<int*>(ch + kBlock);
-  int* hist = flag + 4;
-  float* R = reinterpret_cast<float*>(hist + (nbins + 1) * C);
-
-  for (int i = threadIdx.x; i < (nbins + 1) * C; i += kBlock) hist[i] = 0;
   BinCtx bc;
-  setup_bins<DT>(a, R, tmp, bc, nbins);
-  __syncthreads();
+  FastBin fb;
+  Lds L = setup_lds<DT, C>(smem, a, nbins, bc, fb);
 
   const T* grid = reinterpret_cast<const T*>(a.grid);
   const int64_t nz = a.nz, ny = a.ny, nx = a.nx;
-  const int64_t plane = ny * nx;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lofs = lane & (C - 1);
   constexpr int64_t CHUNK = 64 * VEC;
   const bool vok = vec_ok != 0;
@@ -290,81 +625,20 @@ __global__ __launch_bounds__(kBlock) void hard3d_kernel(HardArgs a, int nbins, i
     if (ys >= ny) continue;
     const int64_t zs = tz * TZ;
     const int64_t ze = zs + TZ < nz ? zs + TZ : nz;
-    const int64_t xb = tx * CHUNK, x0 = xb + lane * VEC;
-
-    int A[TY + 1][VEC], B[TY + 1][VEC];
-    int AL[TY + 1], AR[TY + 1], BL[TY + 1], BR[TY + 1];
-#pragma unroll
-    for (int r = 0; r <= TY; ++r) {
-      const T* row = (ys + r < ny) ? grid + zs * plane + (ys + r) * nx : nullptr;
-      load_keys<DT, VEC>(row, x0, nx, vok, bc, A[r]);
-      AL[r] = load_key1<DT>(row, xb - 1, nx, bc);
-      AR[r] = load_key1<DT>(row, xb + CHUNK, nx, bc);
-    }
-    for (int64_t z = zs; z < ze; ++z) {
-      const bool zn = z + 1 < nz;
-#pragma unroll
-      for (int r = 0; r <= TY; ++r) {
-        const T* row = (zn && ys + r < ny) ? grid + (z + 1) * plane + (ys + r) * nx : nullptr;
-        load_keys<DT, VEC>(row, x0, nx, vok, bc, B[r]);
-        BL[r] = load_key1<DT>(row, xb - 1, nx, bc);
-        BR[r] = load_key1<DT>(row, xb + CHUNK, nx, bc);
-      }
-#pragma unroll
-      for (int r = 0; r < TY; ++r) {
-        if (ys + r < ny) {
-          int s1[VEC], s2[VEC], s3[VEC], s4[VEC];
-#pragma unroll
-          for (int j = 0; j < VEC; ++j) {
-            s1[j] = A[r][j];
-            s2[j] = max(A[r][j], A[r + 1][j]);
-            s3[j] = max(A[r][j], B[r][j]);
-            s4[j] = max(s2[j], max(B[r][j], B[r + 1][j]));
-          }
-          const int e1l = AL[r], e2l = max(AL[r], AL[r + 1]), e3l = max(AL[r], BL[r]),
-                    e4l = max(e2l, max(BL[r], BL[r + 1]));
-          const int e1r = AR[r], e2r = max(AR[r], AR[r + 1]), e3r = max(AR[r], BR[r]),
-                    e4r = max(e2r, max(BR[r], BR[r + 1]));
-          int l1 = __shfl_up(s1[VEC - 1], 1), l2 = __shfl_up(s2[VEC - 1], 1);
-          int l3 = __shfl_up(s3[VEC - 1], 1), l4 = __shfl_up(s4[VEC - 1], 1);
-          int r1 = __shfl_down(s1[0], 1), r2 = __shfl_down(s2[0], 1);
-          int r3 = __shfl_down(s3[0], 1), r4 = __shfl_down(s4[0], 1);
-          if (lane == 0) { l1 = e1l; l2 = e2l; l3 = e3l; l4 = e4l; }
-          if (lane == 63) { r1 = e1r; r2 = e2r; r3 = e3r; r4 = e4r; }
-#pragma unroll
-          for (int j = 0; j < VEC; ++j) {
-            int w1 = tele(j ? s1[j - 1] : l1, s1[j], j + 1 < VEC ? s1[j + 1] : r1);
-            int w2 = -tele(j ? s2[j - 1] : l2, s2[j], j + 1 < VEC ? s2[j + 1] : r2);
-            int w3 = -tele(j ? s3[j - 1] : l3, s3[j], j + 1 < VEC ? s3[j + 1] : r3);
-            int w4 = tele(j ? s4[j - 1] : l4, s4[j], j + 1 < VEC ? s4[j + 1] : r4);
-            // move weights between entries holding the same key
-            if (s4[j] == s3[j]) { w3 += w4; w4 = 0; }
-            else if (s4[j] == s2[j]) { w2 += w4; w4 = 0; }
-            if (s3[j] == s2[j]) { w2 += w3; w3 = 0; }
-            if (s2[j] == s1[j]) { w1 += w2; w2 = 0; }
-            if (s3[j] == s1[j]) { w1 += w3; w3 = 0; }
-            if (w1) atomicAdd(&hist[s1[j] * C + lofs], w1);
-            if (w2) atomicAdd(&hist[s2[j] * C + lofs], w2);
-            if (w3) atomicAdd(&hist[s3[j] * C + lofs], w3);
-            if (w4) atomicAdd(&hist[s4[j] * C + lofs], w4);
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r <= TY; ++r) {
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) A[r][j] = B[r][j];
-        AL[r] = BL[r];
-        AR[r] = BR[r];
-      }
-    }
+    const int64_t xb = tx * CHUNK;
+    if (vok && xb + CHUNK <= nx)
+      tile3d_fast<DT, VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, fb);
+    else
+      tile3d_generic<DT, VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lofs, L.hist, vok, bc, lane);
   }
-  flush_and_finish<DT, C>(a, nbins, hist, tmp, ch, flag);
+  long long* tot = C >= 2 ? reinterpret_cast<long long*>(L.hist) : reinterpret_cast<long long*>(L.R);
+  flush_and_finish<DT, C>(a, nbins, L.hist, L.tmp, L.ch, L.flag, tot);
 }
 
 // ------------------------------------------------------------- launcher
-int copies_for(int nbins) {
-  const int c = 9000 / (nbins + 1);
+int copies_for(int dt, int nbins) {
+  if (dt == 0) return 32;  // uint8: 257 keys, conflict-free layout fits in 33 KB
+  const int c = 4500 / (nbins + 1);
   if (c >= 32) return 32;
   if (c >= 16) return 16;
   if (c >= 8) return 8;
@@ -374,9 +648,8 @@ int copies_for(int nbins) {
 }
 
 size_t lds_bytes(int DT, int nbins, int C, int H) {
-  size_t b = 2 * kBlock * sizeof(long long) + 4 * sizeof(int) + (size_t)(nbins + 1) * C * sizeof(int);
-  if (DT == 1) b += (size_t)H * sizeof(float);
-  return b;
+  size_t a, b, c;
+  return lds_layout(DT, nbins, C, H, &a, &b, &c);
 }
 
 template <int DT, int VEC, int C, int TH>
@@ -451,7 +724,7 @@ hipError_t launch_hard(const HardArgs& a, hipStream_t s) {
     return launch3d<0, 8, 32, 4>(a, 256, s, di);
   }
   const int nbins = a.H;
-  switch (copies_for(nbins)) {
+  switch (copies_for(1, nbins)) {
     case 32: return dispatch_f32<32>(a, nbins, s, di);
     case 16: return dispatch_f32<16>(a, nbins, s, di);
     case 8: return dispatch_f32<8>(a, nbins, s, di);

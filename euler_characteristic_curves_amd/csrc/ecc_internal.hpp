@@ -11,12 +11,15 @@ namespace ecc {
 constexpr int kBlock = 256;        // threads per workgroup (4 waves of 64)
 constexpr int kWavesPerBlock = kBlock / 64;
 constexpr int kAccCopies = 8;      // global accumulator copies, picked by blockIdx % kAccCopies
-constexpr size_t kWsHeader = 256;  // bytes: completion ticket + padding
 
-// Bins of the global accumulator: hard uint8 grids histogram their raw byte
-// value (256 keys), everything else histograms threshold indices (H keys).
+// Bins of the global accumulators: hard uint8 grids histogram their raw byte
+// value (256 keys), everything else threshold indices (H keys).
 __host__ __device__ inline int acc_bins(int H) { return H > 256 ? H : 256; }
 
+// Workspace: [ticket + padding | kAccCopies x acc_bins(H) int64 accumulators].
+// All of it must be zero between calls; the last workgroup of every launch
+// leaves it zero.
+constexpr size_t kWsHeader = 256;
 inline size_t workspace_bytes(int H) {
   return kWsHeader + (size_t)kAccCopies * (size_t)acc_bins(H) * sizeof(long long);
 }

@@ -21,8 +21,8 @@
 // with the first factor computed once per term and the second once per
 // threshold (c is the middle of the threshold range; used when both factors
 // stay inside the float range, else every pair takes exp2 directly).
-// Sums are float64 per lane and per workgroup (LDS), and workgroups combine in
-// 64-bit fixed point so the result is independent of scheduling.
+// Sums are float64 per lane and per workgroup (LDS); workgroups combine in
+// 64-bit fixed point, so the result is independent of scheduling.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -233,29 +233,17 @@ __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles
     __syncthreads();
   }
 
-  // ---------------- combine workgroups in fixed point
-  unsigned int* ticket = reinterpret_cast<unsigned int*>(p.ws);
-  long long* gacc = reinterpret_cast<long long*>(reinterpret_cast<char*>(p.ws) + kWsHeader);
-  const int stride = acc_bins(H);
-  const double scale = ldexp(1.0, fx_shift);
-  long long* mine = gacc + (size_t)(blockIdx.x % kAccCopies) * stride;
+  // ---------------- combine workgroups in 64-bit fixed point (order-free)
   __syncthreads();
-  for (int k = tid; k < H; k += kBlock) {
-    const long long q = __double2ll_rn(accS[k] * scale);
-    if (q != 0) agent_add(mine + k, q);
-  }
-  if (!last_block_arrives(ticket, &misc[1])) return;
+  const double scale = ldexp(1.0, fx_shift);
+  long long* tot = reinterpret_cast<long long*>(terms);  // the term list is no longer needed
+  if (!grid_reduce(p.ws, H, H, [&](int k) { return __double2ll_rn(accS[k] * scale); }, tot, &misc[1])) return;
   const double inv = ldexp(1.0, -fx_shift);
   for (int k = tid; k < H; k += kBlock) {
-    long long s = 0;
-#pragma unroll
-    for (int c = 0; c < kAccCopies; ++c) s += agent_load(gacc + (size_t)c * stride + k);
-    double v = (double)s * inv;
+    double v = (double)tot[k] * inv;
     if constexpr (BWD) v *= (double)p.lambda * (double)p.grad_out[k];
     p.out[k] = (float)v;
   }
-  __syncthreads();
-  for (int i = tid; i < kAccCopies * stride; i += kBlock) agent_store(gacc + i, 0LL);
 }
 
 }  // namespace
@@ -269,7 +257,7 @@ hipError_t launch_soft(const SoftArgs& a, hipStream_t s) {
   int64_t g = (int64_t)di.cus * 4;
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
-  // fixed point: |sum| <= #cells <= 8 * nvox per workgroup partial and in total
+  // fixed point: |partial| and |total| <= #cells <= 8 * nvox, kept below 2^61
   int bits = 0;
   while (bits < 62 && (((int64_t)1) << bits) < 8 * nvox + 8) ++bits;
   int shift = 61 - bits;

@@ -99,9 +99,10 @@ int ecc_hard_3d(const void* grid, int dtype, int64_t nz, int64_t ny, int64_t nx,
  *   tau     device float32[H]; lambda > 0 and finite (inverse temperature)
  *   out     device float32[H]: out[k] = sum_c (-1)^dim(c) *
  *           sigmoid(lambda * (tau_k - value(c))), sigmoid(z) = 1/(1+exp(-z)).
- * Sigmoids are evaluated in float32, summed in float64 per workgroup and
- * combined across workgroups in 64-bit fixed point, so the result does not
- * depend on scheduling.  One kernel launch.
+ * Sigmoids are evaluated in float32 and summed in float64 per workgroup;
+ * workgroup sums are combined in 64-bit fixed point (resolution 2^-s with
+ * s = min(40, 61 - ceil(log2(8*voxels+8))), e.g. 2^-33 at 256^3), so the result
+ * does not depend on scheduling.  One kernel launch.
  */
 int ecc_soft_fwd(const float* grid, int32_t ndim, const int64_t* shape, const float* tau, int32_t H,
                  float lambda, float* out, void* ws, size_t ws_bytes, void* stream);

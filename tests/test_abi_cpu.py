@@ -66,7 +66,7 @@ def test_workspace_bytes(L):
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 
-def hard2d(L, grid=FAKE, dtype=1, ny=4, nx=4, tau=FAKE, H=4, out=FAKE, ws=FAKE, wsb=1 << 20):
+def hard2d(L, grid=FAKE, dtype=1, ny=4, nx=4, tau=FAKE, H=4, out=FAKE, ws=FAKE, wsb=1 << 30):
     return L.lib.ecc_hard_2d(grid, dtype, ny, nx, tau, H, out, ws, wsb, None)
 
 
@@ -85,13 +85,13 @@ def test_hard_argument_errors(L):
     assert hard2d(L, ws=None) == L.ECC_E_WORKSPACE
     assert hard2d(L, wsb=100) == L.ECC_E_WORKSPACE
     assert b"needs" in L.lib.ecc_last_error()
-    r = L.lib.ecc_hard_3d(FAKE, 0, 0, 4, 4, FAKE, 4, FAKE, FAKE, 1 << 20, None)
+    r = L.lib.ecc_hard_3d(FAKE, 0, 0, 4, 4, FAKE, 4, FAKE, FAKE, 1 << 30, None)
     assert r == L.ECC_E_SHAPE
-    r = L.lib.ecc_hard_3d(FAKE, 0, 1 << 14, 1 << 14, 1 << 14, FAKE, 4, FAKE, FAKE, 1 << 20, None)
+    r = L.lib.ecc_hard_3d(FAKE, 0, 1 << 14, 1 << 14, 1 << 14, FAKE, 4, FAKE, FAKE, 1 << 30, None)
     assert r == L.ECC_E_SHAPE
 
 
-def soft(L, ndim=3, shape=(4, 4, 4), lam=1.0, H=4, grid=FAKE, tau=FAKE, out=FAKE, ws=FAKE, wsb=1 << 20,
+def soft(L, ndim=3, shape=(4, 4, 4), lam=1.0, H=4, grid=FAKE, tau=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30,
          bwd=False, gout=FAKE):
     arr = (ctypes.c_int64 * max(1, len(shape)))(*shape) if shape is not None else None
     sp = ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None
