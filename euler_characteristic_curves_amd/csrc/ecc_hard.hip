@@ -238,12 +238,26 @@ template <> struct RawRow<1, 4> { float4 v; float l, r; };
 // Loads are unconditional: callers clamp the row pointer to a valid row and
 // the edge columns to valid columns, and apply validity when forming keys, so
 // the compiler can keep several loads in flight across loop iterations.
+// A 64-bit integer that is the same in every lane, moved to scalar registers
+// (offsets only: a pointer round-tripped through an integer would lose its
+// global address space and turn loads into flat loads).
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const unsigned int lo = __builtin_amdgcn_readfirstlane((unsigned int)(unsigned long long)v);
+  const unsigned int hi = __builtin_amdgcn_readfirstlane((unsigned int)((unsigned long long)v >> 32));
+  return (int64_t)(((unsigned long long)hi << 32) | lo);
+}
+
 template <int DT, int VEC>
 __device__ __forceinline__ void fetch_row(RawRow<DT, VEC>& raw, const typename Elem<DT>::T* row,
                                           int64_t xb, int lane, int64_t xl, int64_t xr) {
-  if constexpr (DT == 0 && VEC == 16) raw.v = *reinterpret_cast<const uint4*>(row + xb + lane * VEC);
-  if constexpr (DT == 0 && VEC == 8) raw.v = *reinterpret_cast<const uint2*>(row + xb + lane * VEC);
-  if constexpr (DT == 1) raw.v = *reinterpret_cast<const float4*>(row + xb + lane * VEC);
+  using T = typename Elem<DT>::T;
+  // wave-uniform base (scalar registers) + 32-bit per-lane byte offset, so the
+  // load uses the saddr + voffset form instead of per-lane 64-bit adds
+  const char* base = reinterpret_cast<const char*>(row + xb);
+  const unsigned int off = (unsigned int)lane * (unsigned int)(VEC * sizeof(T));
+  if constexpr (DT == 0 && VEC == 16) raw.v = *reinterpret_cast<const uint4*>(base + off);
+  if constexpr (DT == 0 && VEC == 8) raw.v = *reinterpret_cast<const uint2*>(base + off);
+  if constexpr (DT == 1) raw.v = *reinterpret_cast<const float4*>(base + off);
   raw.l = row[xl];
   raw.r = row[xr];
 }
@@ -268,6 +282,31 @@ __device__ __forceinline__ int fkey(typename Elem<DT>::T v, const FastBin& fb) {
 // Keys of a fetched row.  The loaded registers are always consumed (validity
 // is applied afterwards with selects), so no load is left pending on any
 // path.  CHECK=false skips the selects for rows known to be inside the grid.
+// Fast bin guess for one float (first k with v <= R[k] when the thresholds
+// are close to uniform): 4 VALU ops, clamped to [0, H] (NaN -> 0).
+__device__ __forceinline__ int bin_guess(float v, const FastBin& fb) {
+  const int k = (int)ceilf(fmaf(v, fb.mul, fb.add));
+  return min(max(k, 0), fb.H);
+}
+
+// Exact check of a guessed bin against the pair table; fixes it by binary
+// search when wrong.  Inlined, but reached only on a wave-uniform slow path.
+__device__ __forceinline__ int bin_fix(float v, int k, const FastBin& fb) {
+  const float2 p = fb.P[k];
+  if (p.x < v && v <= p.y) return k;
+  int lo = 0, hi = fb.H;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (v <= fb.R[mid]) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Keys of a fetched row.  The loaded registers are always consumed (validity
+// is applied afterwards with selects), so no load is left pending on any
+// path.  CHECK=false skips the selects for rows known to be inside the grid.
+// Float rows: every value takes one pair-table read; if any guess of the wave
+// is wrong, one branch fixes all six of the lane's keys.
 template <int DT, int VEC, bool CHECK = true>
 __device__ __forceinline__ void row_keys(const RawRow<DT, VEC>& raw, bool valid, bool has_l, bool has_r,
                                          int trash, const FastBin& fb, int (&k)[VEC], int& kl, int& kr) {
@@ -277,14 +316,32 @@ __device__ __forceinline__ void row_keys(const RawRow<DT, VEC>& raw, bool valid,
     else { w[0] = raw.v.x; w[1] = raw.v.y; }
 #pragma unroll
     for (int j = 0; j < VEC; ++j) k[j] = (int)((w[j >> 2] >> (8 * (j & 3))) & 0xffu);
+    kl = (int)raw.l;
+    kr = (int)raw.r;
   } else {
-    k[0] = fkey<DT>(raw.v.x, fb);
-    k[1] = fkey<DT>(raw.v.y, fb);
-    k[2] = fkey<DT>(raw.v.z, fb);
-    k[3] = fkey<DT>(raw.v.w, fb);
+    // the left edge value is only needed by lane 0 and the right one by lane
+    // 63, so both share one binning slot
+    const bool lane0 = (threadIdx.x & 63) == 0;
+    const float v[5] = {raw.v.x, raw.v.y, raw.v.z, raw.v.w, lane0 ? raw.l : raw.r};
+    int g[5];
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      g[j] = bin_guess(v[j], fb);
+      const float2 p = fb.P[g[j]];
+      ok = ok && (p.x < v[j]) && (v[j] <= p.y);
+    }
+    if (!ok) {
+#pragma unroll
+      for (int j = 0; j < 5; ++j) g[j] = bin_fix(v[j], g[j], fb);
+    }
+    k[0] = g[0];
+    k[1] = g[1];
+    k[2] = g[2];
+    k[3] = g[3];
+    kl = g[4];
+    kr = g[4];
   }
-  kl = fkey<DT>(raw.l, fb);
-  kr = fkey<DT>(raw.r, fb);
   if constexpr (CHECK) {
 #pragma unroll
     for (int j = 0; j < VEC; ++j) k[j] = valid ? k[j] : trash;
@@ -523,11 +580,11 @@ __device__ __forceinline__ void tile3d_fast(const typename Elem<DT>::T* grid, in
   const bool has_l = xb > 0, has_r = xb + CHUNK < nx;
   const int64_t xl = has_l ? xb - 1 : xb, xr = has_r ? xb + CHUNK : xb;
   using T = typename Elem<DT>::T;
-  int64_t roff[TY + 1];
+  int64_t roff[TY + 1];  // element offsets of the rows in plane 0 (scalar registers)
 #pragma unroll
-  for (int r = 0; r <= TY; ++r) roff[r] = (ys + r < ny ? ys + r : ny - 1) * nx;
+  for (int r = 0; r <= TY; ++r) roff[r] = uni64((ys + r < ny ? ys + r : ny - 1) * nx);
   auto rowp = [&](int64_t z, int r) -> const T* {
-    return grid + (z < nz ? z : nz - 1) * plane + roff[r];
+    return grid + uni64((z < nz ? z : nz - 1) * plane + roff[r]);
   };
   RawRow<DT, VEC> raw[TY + 1];
   int A[TY + 1][VEC], AL[TY + 1], AR[TY + 1], B[TY + 1][VEC], BL[TY + 1], BR[TY + 1];
@@ -538,20 +595,27 @@ __device__ __forceinline__ void tile3d_fast(const typename Elem<DT>::T* grid, in
 #pragma unroll
   for (int r = 0; r <= TY; ++r) fetch_row<DT, VEC>(raw[r], rowp(zs + 1, r), xb, lane, xl, xr);
   const bool rows_in = ys + TY < ny;
+  // One plane step: keys of plane z+1 into Y (from the raw rows fetched one
+  // step earlier), fetch of plane z+2, then the rows of plane z (X) against
+  // plane z+1 (Y).  (Unrolling twice to swap X and Y instead of copying was
+  // measured slower: the doubled loop body costs more than the moves.)
+#define ECC_PLANE_STEP(X, XL, XR, Y, YL, YR, ZZ)                                              \
+  {                                                                                           \
+    const bool zn = (ZZ) + 1 < nz;                                                            \
+    if (zn && rows_in) {                                                                      \
+      _Pragma("unroll") for (int r = 0; r <= TY; ++r)                                         \
+        row_keys<DT, VEC, false>(raw[r], true, has_l, has_r, trash, fb, Y[r], YL[r], YR[r]);   \
+    } else {                                                                                  \
+      _Pragma("unroll") for (int r = 0; r <= TY; ++r)                                         \
+        row_keys<DT, VEC, true>(raw[r], zn && ys + r < ny, has_l, has_r, trash, fb, Y[r],      \
+                                YL[r], YR[r]);                                                \
+    }                                                                                         \
+    _Pragma("unroll") for (int r = 0; r <= TY; ++r)                                           \
+      fetch_row<DT, VEC>(raw[r], rowp((ZZ) + 2, r), xb, lane, xl, xr);                        \
+    rows3d<DT, VEC, C, TY>(X, XL, XR, Y, YL, YR, ys, ny, hist, lofs);                         \
+  }
   for (int64_t z = zs; z < ze; ++z) {
-    const bool zn = z + 1 < nz;
-    if (zn && rows_in) {
-#pragma unroll
-      for (int r = 0; r <= TY; ++r)
-        row_keys<DT, VEC, false>(raw[r], true, has_l, has_r, trash, fb, B[r], BL[r], BR[r]);
-    } else {
-#pragma unroll
-      for (int r = 0; r <= TY; ++r)
-        row_keys<DT, VEC, true>(raw[r], zn && ys + r < ny, has_l, has_r, trash, fb, B[r], BL[r], BR[r]);
-    }
-#pragma unroll
-    for (int r = 0; r <= TY; ++r) fetch_row<DT, VEC>(raw[r], rowp(z + 2, r), xb, lane, xl, xr);
-    rows3d<DT, VEC, C, TY>(A, AL, AR, B, BL, BR, ys, ny, hist, lofs);
+    ECC_PLANE_STEP(A, AL, AR, B, BL, BR, z)
 #pragma unroll
     for (int r = 0; r <= TY; ++r) {
 #pragma unroll
@@ -560,6 +624,7 @@ __device__ __forceinline__ void tile3d_fast(const typename Elem<DT>::T* grid, in
       AR[r] = BR[r];
     }
   }
+#undef ECC_PLANE_STEP
 }
 
 template <int DT, int VEC, int C, int TY>
