@@ -7,10 +7,13 @@ Inputs are resident in HBM before timing; the 8192^2 input rotates over 8
 distinct buffers (512 MiB in all) and the 512^3 input over 2, so repeated
 steps cannot be served from the 256 MB Infinity Cache.
 
-Also reported on the same JSON line: per-kernel durations and roofline of
-each hard kernel (HIP events on the launch stream), the soft forward /
-backward at 256^3 (H=256, lambda=50), and the CPU oracle timed on a bounded
-sample of the same workloads (cpu_baseline).
+Also reported on the same JSON line: per-kernel durations (mean of
+back-to-back launches, and min / median of individually timed launches, HIP
+events on the launch stream) and the roofline of each hard kernel; the other
+grid sizes (128^2, 1024^2, 1024^3) as context; the soft forward / backward at
+256^3 (H=256, lambda=50) with their VALU-issue fraction; and the CPU oracle
+timed on a bounded sample of the same workloads (cpu_baseline), on one core
+and on all cores, before the GPU is touched.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -28,7 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public spec
-VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9   # non-packed 32-bit lane-ops/s: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+VALU_WAVE_INSTR_PEAK = 256 * 2.4e9    # wave64 VALU instructions/s: one per CU per clock (4 SIMD x 16 lanes)
 
 
 def n_cells(shape):
@@ -43,6 +46,103 @@ def n_cells(shape):
     return total
 
 
+KERNEL_SOURCES = ("euler_characteristic_curves_amd/csrc/ecc_hard.hip",
+                  "euler_characteristic_curves_amd/csrc/ecc_device.hpp",
+                  "euler_characteristic_curves_amd/csrc/ecc_internal.hpp")
+TRAFFIC_PROFILE = "profiles/hard3d_512cube_f32_traffic.md"
+SOFT_SOURCES = ("euler_characteristic_curves_amd/csrc/ecc_soft.hip",
+                "euler_characteristic_curves_amd/csrc/ecc_device.hpp",
+                "euler_characteristic_curves_amd/csrc/ecc_internal.hpp")
+SQ_PROFILE = "profiles/ecc_kernels_bench_sq_counters.md"
+
+
+def source_hash(files):
+    """sha256 over the given kernel sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in files:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def kernel_source_hash():
+    """sha256 over the sources the hard kernels are built from."""
+    return source_hash(KERNEL_SOURCES)
+
+
+def profile_fields(rel):
+    """`name: value` lines of a committed profile summary (backticks stripped)."""
+    path = os.path.join(ROOT, rel)
+    fields = {}
+    if not os.path.exists(path):
+        return fields
+    with open(path) as f:
+        for line in f:
+            t = line.strip()
+            if t and ":" in t and not t.startswith(("#", "|", "`")) and " " not in t.split(":", 1)[0]:
+                k, v = t.split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    return fields
+
+
+def recorded_traffic():
+    """HBM bytes per hard3d launch from the committed rocprofv3 --pmc profile.
+
+    Returns None unless the profile was taken on the current kernel sources
+    (its `kernel_source_sha256:` line matches), so a stale figure is never
+    reported.
+    """
+    fields = profile_fields(TRAFFIC_PROFILE)
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def recorded_soft_valu():
+    """(forward, backward) VALU wave-instructions per soft launch at 256^3, H=256.
+
+    The count is fixed by the kernel and its input; it comes from the committed
+    rocprofv3 SQ_INSTS_VALU profile and is used only while the soft sources
+    hash to the value recorded there.
+    """
+    fields = profile_fields(SQ_PROFILE)
+    if fields.get("soft_source_sha256") != source_hash(SOFT_SOURCES):
+        return None, None
+    try:
+        return float(fields["soft_fwd_valu_wave_instr"]), float(fields["soft_bwd_valu_wave_instr"])
+    except (KeyError, ValueError):
+        return None, None
+
+
+def traffic_run():
+    """Workload for the two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE).
+
+    Runs a plain 512 MiB device-to-device copy (the calibration kernel of
+    known size) three times, then the hard 3D kernel on the 512^3 float32
+    field three times.
+    """
+    import torch
+
+    import euler_characteristic_curves_amd as E
+    from euler_characteristic_curves_amd import workloads as W
+    dev = torch.device("cuda:0")
+    g4, t4, _ = W.make_workload("c4a_512cube_f32_grf")
+    d4 = torch.from_numpy(g4).to(dev)
+    dst = torch.empty_like(d4)
+    dt4 = torch.from_numpy(t4).to(dev)
+    for _ in range(3):
+        dst.copy_(d4)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        E.ecc_hard_3d(d4, dt4)
+    torch.cuda.synchronize()
+    print("traffic run done: copy bytes", d4.numel() * 4, flush=True)
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -50,17 +150,20 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--kernel-reps", type=int, default=40)
-    ap.add_argument("--soft-reps", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--soft-reps", type=int, default=5)
     ap.add_argument("--no-soft", action="store_true")
+    ap.add_argument("--no-context", action="store_true", help="skip the 128^2 / 1024^2 / 1024^3 timings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="only run the workload profiled for HBM traffic (under rocprofv3 --pmc)")
     return ap.parse_args()
 
 
 def timed(torch, fn, reps):
-    """Average ms per call of fn() over reps calls, HIP events on torch's current stream."""
+    """Mean ms per call of fn(i) over reps back-to-back calls (HIP events on the current stream)."""
     s = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -73,23 +176,88 @@ def timed(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def cpu_baseline(W, oracle):
-    """The oracle on a bounded sample of the same two workloads, on this host."""
-    g3, t3, _ = W.make_workload("c3_8192sq_u8")
-    s3 = np.ascontiguousarray(g3[:1024])
-    g4, t4, _ = W.make_workload("c4a_512cube_f32_grf")
-    s4 = np.ascontiguousarray(g4[:32])
+def timed_each(torch, fn, reps):
+    """(min, median) ms of reps individually bracketed calls of fn(i)."""
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(s)
+        fn(i)
+        b.record(s)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[0], t[len(t) // 2]
+
+
+# ------------------------------------------------------------ CPU baseline
+_CPU = {}
+
+
+def _cpu_work(i):
+    """One worker's share of the all-core oracle run: a 1024-row band of the
+    8192^2 grid and a 32-plane slab of the 512^3 field (hard ECC of each)."""
+    import oracle
+    g3, t3, g4, t4 = _CPU["g3"], _CPU["t3"], _CPU["g4"], _CPU["t4"]
+    r = (i % 8) * 1024
+    z = (i % 16) * 32
+    oracle.ecc_hard(np.ascontiguousarray(g3[r:r + 1024]), t3)
+    oracle.ecc_hard(np.ascontiguousarray(g4[z:z + 32]), t4)
+    return 1024 * g3.shape[1] + 32 * g4.shape[1] * g4.shape[2]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(W, g3, t3, g4, t4):
+    """The oracle on a bounded sample of the two bench workloads, on this host.
+
+    Runs before anything touches the GPU (the all-core leg forks workers).
+    One core: rows 0..4095 of the 8192^2 grid and planes 0..127 of the 512^3
+    field.  All cores: one worker per available core (at most 16), each on a
+    1024-row band and a 32-plane slab (histograms of disjoint owners add, so
+    this is the oracle's natural parallel form); throughput = voxels / wall.
+    """
+    import multiprocessing as mp
+
+    import oracle
+    s3 = np.ascontiguousarray(g3[:4096])
+    s4 = np.ascontiguousarray(g4[:128])
     t0 = time.perf_counter()
     oracle.ecc_hard(s3, t3)
     t1 = time.perf_counter()
     oracle.ecc_hard(s4, t4)
     t2 = time.perf_counter()
-    vox = s3.size + s4.size
+    one = (s3.size + s4.size) / (t2 - t0)
+
+    try:
+        ncores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncores = os.cpu_count() or 1
+    ncores = max(1, min(ncores, 16))
+    _CPU.update(g3=g3, t3=t3, g4=g4, t4=t4)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(ncores) as pool:
+        t3a = time.perf_counter()
+        vox = sum(pool.map(_cpu_work, range(ncores)))
+        t4a = time.perf_counter()
+    _CPU.clear()
     return {
-        "value": vox / (t2 - t0), "unit": "voxels/s", "cores": 1, "kind": "oracle",
-        "sample": f"rows 0..1023 of the 8192^2 uint8 grid ({s3.size} px, {t1 - t0:.1f} s) + planes 0..31 "
+        "value": one, "unit": "voxels/s", "cores": 1, "kind": "oracle",
+        "sample": f"rows 0..4095 of the 8192^2 uint8 grid ({s3.size} px, {t1 - t0:.1f} s) + planes 0..127 "
                   f"of the 512^3 GRF ({s4.size} vox, {t2 - t1:.1f} s); numpy, single-threaded",
-        "host_cpus": os.cpu_count(),
+        "all_cores": {"value": vox / (t4a - t3a), "unit": "voxels/s", "cores": ncores,
+                      "sample": f"{ncores} workers, each a 1024-row band of the 8192^2 grid + a 32-plane slab "
+                                f"of the 512^3 GRF ({vox} voxels in {t4a - t3a:.1f} s wall)"},
+        "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
     }
 
 
@@ -102,20 +270,31 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.traffic_run:
+        traffic_run()
+        return
+
+    from euler_characteristic_curves_amd import workloads as W
+
+    log("generating 8192^2 uint8 grid")
+    g3, t3, _ = W.make_workload("c3_8192sq_u8")
+    log("generating 512^3 float32 GRF")
+    g4, t4, _ = W.make_workload("c4a_512cube_f32_grf")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample, before the GPU is touched)")
+        cpu = cpu_baseline(W, g3, t3, g4, t4)
+
     import torch
 
     import euler_characteristic_curves_amd as E
-    from euler_characteristic_curves_amd import workloads as W
 
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
 
-    log("generating 8192^2 uint8 grid")
-    g3, t3, _ = W.make_workload("c3_8192sq_u8")
-    log("generating 512^3 float32 GRF")
-    g4, t4, _ = W.make_workload("c4a_512cube_f32_grf")
     n3, n4 = g3.size, g4.size
     b3 = [torch.from_numpy(g3).to(dev) for _ in range(8)]
     d4 = torch.from_numpy(g4).to(dev)
@@ -137,12 +316,37 @@ def main():
     ms_step = timed(torch, step, args.steps)
 
     log("per-kernel timing")
-    ms3 = timed(torch, lambda i: E.ecc_hard_2d(b3[i % 8], dt3, out=o3), args.kernel_reps)
-    ms4 = timed(torch, lambda i: E.ecc_hard_3d(b4[i % 2], dt4, out=o4), args.kernel_reps)
+    f3 = lambda i: E.ecc_hard_2d(b3[i % 8], dt3, out=o3)
+    f4 = lambda i: E.ecc_hard_3d(b4[i % 2], dt4, out=o4)
+    ms3, ms4 = timed(torch, f3, args.kernel_reps), timed(torch, f4, args.kernel_reps)
+    mm3, mm4 = timed_each(torch, f3, args.kernel_reps), timed_each(torch, f4, args.kernel_reps)
     alg3 = n3 * 1 + 4 * 256 + 8 * 256
     alg4 = n4 * 4 + 4 * 512 + 8 * 512
     gbs3 = alg3 / (ms3 * 1e-3) / 1e9
     gbs4 = alg4 / (ms4 * 1e-3) / 1e9
+    del b3
+    torch.cuda.empty_cache()
+
+    context = None
+    if not args.no_context:
+        context = {"rtx_a6000_ms_from_the_pages": {"1024sq": 0.032, "8192sq": 1.6, "512cube": 5.61,
+                                                   "1024cube": 48.47}}
+        for name in ("c1_128sq_f32", "c2_1024sq_f32_grf", "c4b_1024cube_f32"):
+            log("context", name)
+            g, tau, _ = W.make_workload(name)
+            dg, dtau = torch.from_numpy(g).to(dev), torch.from_numpy(tau).to(dev)
+            del g
+            o = torch.empty(dtau.numel(), dtype=torch.int64, device=dev)
+            fn = lambda i: E.ecc_hard(dg, dtau, out=o)
+            fn(0)
+            reps = 10 if dg.numel() > 1e8 else args.kernel_reps
+            ms = timed(torch, fn, reps)
+            mn, md = timed_each(torch, fn, reps)
+            context[name] = {"shape": list(dg.shape), "H": int(dtau.numel()), "ms": ms, "min_ms": mn,
+                             "median_ms": md, "voxels_per_s": dg.numel() / (ms * 1e-3),
+                             "GB_s": (dg.numel() * dg.element_size() + 12 * dtau.numel()) / (ms * 1e-3) / 1e9}
+            del dg, dtau, o
+            torch.cuda.empty_cache()
 
     soft = None
     if not args.no_soft:
@@ -156,18 +360,17 @@ def main():
         msf = timed(torch, lambda i: E.ecc_soft_fwd(dgs, dts, lam), args.soft_reps)
         msb = timed(torch, lambda i: E.ecc_soft_bwd_tau(dgs, dts, lam, dgo), args.soft_reps)
         pairs = n_cells(gs.shape) * ts.size
+        vf, vb = recorded_soft_valu()
         soft = {
             "workload": "soft ECC 256^3 float32 uniform, H=256, lambda=50",
-            "fwd_ms": msf, "bwd_ms": msb,
+            "fwd_ms": msf, "bwd_ms": msb, "fwd_plus_bwd_ms": msf + msb,
             "cell_threshold_pairs": pairs,
             "fwd_pairs_per_s": pairs / (msf * 1e-3), "bwd_pairs_per_s": pairs / (msb * 1e-3),
+            "roofline": {"bound": "valu", "unit": "wave64 VALU instr/s", "peak": VALU_WAVE_INSTR_PEAK,
+                         "fwd_frac": None if vf is None else vf / (msf * 1e-3) / VALU_WAVE_INSTR_PEAK,
+                         "bwd_frac": None if vb is None else vb / (msb * 1e-3) / VALU_WAVE_INSTR_PEAK,
+                         "valu_instr_per_launch": {"fwd": vf, "bwd": vb}},
         }
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle on a bounded sample)")
-        import oracle
-        cpu = cpu_baseline(W, oracle)
 
     vox_step = n3 + n4
     line = {
@@ -191,19 +394,21 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": gbs4, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": gbs4 / HBM_PEAK_GBS, "traffic": None,
+            "frac": gbs4 / HBM_PEAK_GBS, "traffic": recorded_traffic(),
             "kernel": "hard3d_kernel (512^3 float32, H=512)", "ms_per_launch": ms4,
             "algorithmic_bytes_per_launch": alg4,
         },
         "kernels": {
-            "hard_8192sq_u8": {"ms": ms3, "voxels_per_s": n3 / (ms3 * 1e-3), "GB_s": gbs3,
+            "hard_8192sq_u8": {"ms": ms3, "min_ms": mm3[0], "median_ms": mm3[1],
+                               "voxels_per_s": n3 / (ms3 * 1e-3), "GB_s": gbs3,
                                "frac_hbm_peak": gbs3 / HBM_PEAK_GBS, "algorithmic_bytes": alg3},
-            "hard_512cube_f32": {"ms": ms4, "voxels_per_s": n4 / (ms4 * 1e-3), "GB_s": gbs4,
+            "hard_512cube_f32": {"ms": ms4, "min_ms": mm4[0], "median_ms": mm4[1],
+                                 "voxels_per_s": n4 / (ms4 * 1e-3), "GB_s": gbs4,
                                  "frac_hbm_peak": gbs4 / HBM_PEAK_GBS, "algorithmic_bytes": alg4},
         },
         "soft": soft,
         "cpu_baseline": cpu,
-        "context": {"rtx_a6000_ms": {"8192sq": 1.6, "512cube": 5.61, "1024sq": 0.032, "1024cube": 48.47}},
+        "context": context,
     }
     print(json.dumps(line), flush=True)
 

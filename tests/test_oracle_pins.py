@@ -5,7 +5,9 @@ computed a different way: explicit per-cell counting, union-find Betti
 numbers, scipy.ndimage labelling, hand-derived worked examples or closed forms.
 """
 
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -26,40 +28,20 @@ def _all_thresholds(g):
 
 
 # ------------------------------------------------------------------ hand-worked
-def _with(a, idx, v):
-    a[idx] = v
-    return a
-
-
-# Each case was counted by hand from the definition (cells of the V-construction
-# complex whose corners are all <= tau; chi = V - E + F - C).
-HAND_CASES = [
-    # 3x3 ring of 2s with 0 corners and a 3 in the middle.
-    # tau=0: four isolated corners -> 4.  tau=2: 8 pixels, 8 edges, no square
-    # (each square holds the centre) -> 0 (one loop).  tau=3: full 3x3 box:
-    # 9 - 12 + 4 = 1.
-    (np.array([[0, 2, 0], [2, 3, 2], [0, 2, 0]], np.float32),
-     [-1, 0, 1, 2, 2.5, 3, 4], [0, 4, 4, 0, 0, 1, 1]),
-    # one row 1 3 0 3 2: tau=0 -> {0}; tau=1 -> {1},{0}; tau=2 -> three
-    # separated pixels; tau=3 -> 5 vertices, 4 edges -> 1.
-    (np.array([[1, 3, 0, 3, 2]], np.float32), [0, 1, 2, 3], [1, 2, 3, 1]),
-    # diagonal zeros are not joined (no diagonal edges): 2; then the box: 4-4+1.
-    (np.array([[0, 1], [1, 0]], np.float32), [0, 1], [2, 1]),
-    # 3x3x3 zeros with a 5 at the centre: at tau=0 the 26 outer voxels span
-    # 48 edges (54 minus the 6 at the centre), 24 squares (36 minus 12) and no
-    # cube (all 8 hold the centre): 26 - 48 + 24 = 2, a sphere.
-    (_with(np.zeros((3, 3, 3), np.float32), (1, 1, 1), 5), [-1, 0, 5], [0, 2, 1]),
-    # 3x3x3 zeros with the centre column (x=1,y=1, all z) at 5: 24 voxels,
-    # 54-14 = 40 edges, 36-20 = 16 squares, 0 cubes: 24 - 40 + 16 = 0, a solid torus.
-    (_with(np.zeros((3, 3, 3), np.float32), (slice(None), 1, 1), 5), [0, 5], [0, 1]),
-]
+# Worked examples counted by hand from the definition, stored with their
+# derivations in tests/golden/hand_worked.json.
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_worked.json")
+with open(GOLDEN) as _f:
+    HAND_CASES = json.load(_f)["cases"]
 
 
 @pytest.mark.parametrize("case", range(len(HAND_CASES)))
 def test_hand_worked_examples(case):
-    g, tau, want = HAND_CASES[case]
+    c = HAND_CASES[case]
+    g = np.array(c["grid"], np.float32)
+    tau, want = c["tau"], c["ecc"]
     got = oracle.ecc_hard(g, np.array(tau, np.float32))
-    assert got.tolist() == want
+    assert got.tolist() == want, c["name"]
     for t, w in zip(tau, want):
         assert oracle.ecc_at(g, t) == w
         assert pins.brute_chi(g, t) == w
