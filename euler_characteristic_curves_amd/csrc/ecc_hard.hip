@@ -289,11 +289,10 @@ __device__ __forceinline__ int bin_guess(float v, const FastBin& fb) {
   return min(max(k, 0), fb.H);
 }
 
-// Exact check of a guessed bin against the pair table; fixes it by binary
-// search when wrong.  Inlined, but reached only on a wave-uniform slow path.
-__device__ __forceinline__ int bin_fix(float v, int k, const FastBin& fb) {
-  const float2 p = fb.P[k];
-  if (p.x < v && v <= p.y) return k;
+// Exact bin by binary search over the running max; reached only on the slow
+// path of a wave in which some guess failed its check (nothing from the fast
+// check is reused, so none of it is kept live for this path).
+__device__ __forceinline__ int bin_fix(float v, const FastBin& fb) {
   int lo = 0, hi = fb.H;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
@@ -323,17 +322,19 @@ __device__ __forceinline__ void row_keys(const RawRow<DT, VEC>& raw, bool valid,
     // 63, so both share one binning slot
     const bool lane0 = (threadIdx.x & 63) == 0;
     const float v[5] = {raw.v.x, raw.v.y, raw.v.z, raw.v.w, lane0 ? raw.l : raw.r};
+    // every check is evaluated (bitwise, not short-circuit) so the five
+    // table reads issue back to back as 64-bit loads with one wait
     int g[5];
     bool ok = true;
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
       g[j] = bin_guess(v[j], fb);
       const float2 p = fb.P[g[j]];
-      ok = ok && (p.x < v[j]) && (v[j] <= p.y);
+      ok = ok & (p.x < v[j]) & (v[j] <= p.y);
     }
     if (!ok) {
 #pragma unroll
-      for (int j = 0; j < 5; ++j) g[j] = bin_fix(v[j], g[j], fb);
+      for (int j = 0; j < 5; ++j) g[j] = bin_fix(v[j], fb);
     }
     k[0] = g[0];
     k[1] = g[1];
@@ -465,39 +466,104 @@ __device__ __forceinline__ void tile2d_generic(const typename Elem<DT>::T* grid,
 struct Lds {
   long long* tmp;
   long long* ch;
-  int* flag;
+  int* flag;   // [0] last-workgroup flag, [1] bucket table usable
   int* hist;
   float* R;
-  float2* P;
+  float2* P;   // pair table, or
+  float2* lut; // bucket table (same LDS)
 };
 
 __host__ __device__ inline size_t align16(size_t b) { return (b + 15) & ~(size_t)15; }
 
-__host__ __device__ inline size_t lds_layout(int DT, int nbins, int C, int H, size_t* off_hist,
-                                             size_t* off_R, size_t* off_P) {
+// LDS: [tmp | ch | flag] (fixed, so the histogram sits at a compile-time
+// offset that folds into every ds_add) | histogram | R | X, where X holds
+// either the bucket table (nlut entries) or, when there is none or it cannot
+// be used, the pair table P (H+1 entries).
+__host__ __device__ inline size_t lds_layout(int DT, int nbins, int C, int H, int nlut, size_t* off_hist,
+                                             size_t* off_R, size_t* off_X) {
   size_t b = 2 * kBlock * sizeof(long long) + 4 * sizeof(int);
   *off_hist = b;
   b = align16(b + (size_t)(nbins + 1) * C * sizeof(int));
   *off_R = b;
   if (DT == 1) b = align16(b + (size_t)H * sizeof(float));
-  *off_P = b;
-  if (DT == 1) b += (size_t)(H + 1) * sizeof(float2);
+  *off_X = b;
+  if (DT == 1) b += (size_t)(nlut > H + 1 ? nlut : H + 1) * sizeof(float2);
   return b;
 }
 
+// ------------------------------------------------------------ bucket table
+// Exact binning with one table read for float grids.  A monotone map
+//     bucket(v) = int(clamp(fma(v, mul, add), 0, n-1))
+// splits the line into n buckets.  If no two thresholds R_k share a bucket,
+// then for v in bucket j every R_k in an earlier bucket is < v and every R_k
+// in a later one is > v, so
+//     bin(v) = #{k : R_k < v} = base[j] + [v > thr[j]],
+// with base[j] = #{k : bucket(R_k) < j} and thr[j] the threshold in bucket j
+// (+inf if none).  The table is built per workgroup from R with the same
+// bucket() code the sweep uses; the flag says whether the thresholds met the
+// one-per-bucket condition (with finite, increasing end points), otherwise
+// the sweep takes the checked path.
+struct LutBin {
+  const float2* lut;  // (thr, base as int bits)
+  float mul, add, hi;
+};
+
+__device__ __forceinline__ int lut_bucket(float v, const LutBin& lb) {
+  return (int)__builtin_amdgcn_fmed3f(fmaf(v, lb.mul, lb.add), 0.0f, lb.hi);
+}
+
+__device__ __forceinline__ int lut_key(float v, const LutBin& lb) {
+  const float2 e = lb.lut[lut_bucket(v, lb)];
+  return __float_as_int(e.y) + (int)(v > e.x);
+}
+
+__device__ __forceinline__ void build_lut(const float* R, int H, int n, float2* lut, int* ok_flag,
+                                          LutBin& lb) {
+  const float lo = R[0], hi = R[H - 1];
+  const float INF = __builtin_inff();
+  float mul = 0.0f, add = 0.0f;
+  bool ok = H >= 2 && lo > -INF && hi < INF && hi > lo;
+  if (ok) {
+    mul = (float)(n - 1) / (hi - lo);
+    add = -lo * mul;
+    ok = mul > 0.0f && mul < INF && add > -INF && add < INF;
+  }
+  if (!ok) { mul = 0.0f; add = 0.0f; }
+  lb.mul = mul;
+  lb.add = add;
+  lb.hi = (float)(n - 1);
+  lb.lut = lut;
+  if (threadIdx.x == 0) *ok_flag = ok ? 1 : 0;
+  __syncthreads();
+  if (!*ok_flag) return;  // uniform: every thread read the same flag
+  bool mine = true;
+  for (int k = threadIdx.x; k <= H; k += kBlock) {
+    const int bprev = k > 0 ? lut_bucket(R[k - 1], lb) : -1;
+    const int bk = k < H ? lut_bucket(R[k], lb) : n - 1;
+    if (k > 0 && k < H && bk <= bprev) mine = false;
+    for (int j = bprev + 1; j <= bk; ++j)
+      lut[j] = make_float2((k < H && j == bk) ? R[k] : INF, __int_as_float(k));
+  }
+  __syncthreads();
+  if (!mine) *ok_flag = 0;  // benign race: every writer stores 0
+  __syncthreads();
+}
+
 template <int DT, int C>
-__device__ __forceinline__ Lds setup_lds(unsigned char* smem, const HardArgs& a, int nbins, BinCtx& bc,
-                                         FastBin& fb) {
-  size_t oh, oR, oP;
-  lds_layout(DT, nbins, C, a.H, &oh, &oR, &oP);
+__device__ __forceinline__ Lds setup_lds(unsigned char* smem, const HardArgs& a, int nbins, int nlut,
+                                         BinCtx& bc, FastBin& fb, LutBin& lb) {
+  size_t oh, oR, oX;
+  lds_layout(DT, nbins, C, a.H, nlut, &oh, &oR, &oX);
   Lds L;
   L.tmp = reinterpret_cast<long long*>(smem);
   L.ch = L.tmp + kBlock;
   L.flag = reinterpret_cast<int*>(L.ch + kBlock);
   L.hist = reinterpret_cast<int*>(smem + oh);
   L.R = reinterpret_cast<float*>(smem + oR);
-  L.P = reinterpret_cast<float2*>(smem + oP);
+  L.P = reinterpret_cast<float2*>(smem + oX);
+  L.lut = reinterpret_cast<float2*>(smem + oX);
   for (int i = threadIdx.x; i < (nbins + 1) * C; i += kBlock) L.hist[i] = 0;
+  if (threadIdx.x == 0) L.flag[1] = 0;
   setup_bins<DT>(a, L.R, L.tmp, bc, nbins);
   fb.P = L.P;
   fb.R = L.R;
@@ -505,19 +571,27 @@ __device__ __forceinline__ Lds setup_lds(unsigned char* smem, const HardArgs& a,
   fb.mul = bc.scale;
   fb.add = -bc.r0 * bc.scale;
   if (!(fb.add > -__builtin_inff() && fb.add < __builtin_inff())) { fb.mul = 0.0f; fb.add = 0.0f; }
-  if constexpr (DT == 1) build_pairs(L.R, a.H, L.P);
+  lb.lut = L.lut;
+  lb.mul = lb.add = lb.hi = 0.0f;
+  __syncthreads();
+  if constexpr (DT == 1) {
+    if (nlut > 0) build_lut(L.R, a.H, nlut, L.lut, L.flag + 1, lb);
+    // the pair table is only needed when the bucket table is not used
+    if (!L.flag[1]) build_pairs(L.R, a.H, L.P);
+  }
   __syncthreads();
   return L;
 }
 
 template <int DT, int VEC, int C, int TH>
 __global__ __launch_bounds__(kBlock) void hard2d_kernel(HardArgs a, int nbins, int64_t ntx,
-                                                        int64_t ntiles, int vec_ok) {
+                                                        int64_t ntiles, int vec_ok, int th) {
   extern __shared__ __align__(16) unsigned char smem[];
   using T = typename Elem<DT>::T;
   BinCtx bc;
   FastBin fb;
-  Lds L = setup_lds<DT, C>(smem, a, nbins, bc, fb);
+  LutBin lb;
+  Lds L = setup_lds<DT, C>(smem, a, nbins, 0, bc, fb, lb);
 
   const T* grid = reinterpret_cast<const T*>(a.grid);
   const int64_t ny = a.ny, nx = a.nx;
@@ -529,9 +603,9 @@ __global__ __launch_bounds__(kBlock) void hard2d_kernel(HardArgs a, int nbins, i
 
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t tx = t % ntx, tyb = t / ntx;
-    const int64_t ys = (tyb * kWavesPerBlock + wave) * TH;
+    const int64_t ys = (tyb * kWavesPerBlock + wave) * th;
     if (ys >= ny) continue;
-    const int64_t ye = ys + TH < ny ? ys + TH : ny;
+    const int64_t ye = ys + th < ny ? ys + th : ny;
     const int64_t xb = tx * CHUNK;
     if (vok && xb + CHUNK <= nx)
       tile2d_fast<DT, VEC, C>(grid, ny, nx, ys, ye, xb, lane, lofs, L.hist, nbins, fb);
@@ -627,6 +701,82 @@ __device__ __forceinline__ void tile3d_fast(const typename Elem<DT>::T* grid, in
 #undef ECC_PLANE_STEP
 }
 
+// Float interior tile with bucket-table binning (no per-value check).  The
+// wave holds the keys of TY+1 rows (TY plus the one-row y halo) of planes z
+// and z+1 and marches along z; the raw rows of plane z+2 are in flight while
+// plane z is processed.  Each lane also loads one value outside the wave's
+// column chunk: lane 0 the one on the left, every other lane the one on the
+// right (only lane 63 uses it), so one load and one binning serve both edges.
+// Row and plane validity is wave-uniform and handled by branches.  The z loop
+// is unrolled twice so that planes z and z+1 swap roles instead of being copied.
+struct RawLut {
+  float4 v;
+  float e;
+};
+
+template <int VEC, int C, int TY>
+__device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_t ny, int64_t nx, int64_t zs,
+                                           int64_t ze, int64_t ys, int64_t xb, int lane, int lofs, int* hist,
+                                           int trash, const LutBin& lb) {
+  static_assert(VEC == 4, "float rows are loaded as float4");
+  constexpr int64_t CHUNK = 64 * VEC;
+  const int64_t plane = ny * nx;
+  const bool has_l = xb > 0, has_r = xb + CHUNK < nx;
+  const bool lane0 = lane == 0;
+  const bool slot_ok = lane0 ? has_l : has_r;
+  // byte offsets from the element just left of the chunk: vector at 4 + 16 lane,
+  // edge at 0 (left) or 4 (CHUNK + 1) (right); a missing edge reads the chunk's
+  // first element instead (its key is replaced by trash)
+  const unsigned int voff = 4u + 16u * (unsigned int)lane;
+  const unsigned int eoff = lane0 ? (has_l ? 0u : 4u) : (has_r ? 4u * (unsigned int)(CHUNK + 1) : 4u);
+  int64_t roff[TY + 1];
+#pragma unroll
+  for (int r = 0; r <= TY; ++r) roff[r] = uni64((ys + r < ny ? ys + r : ny - 1) * nx + xb - 1);
+  auto fetch = [&](RawLut& q, int64_t z, int r) {
+    const char* base = reinterpret_cast<const char*>(grid + uni64((z < nz ? z : nz - 1) * plane + roff[r]));
+    q.v = *reinterpret_cast<const float4*>(base + voff);
+    q.e = *reinterpret_cast<const float*>(base + eoff);
+  };
+  auto keys = [&](const RawLut& q, bool row_ok, int (&k)[VEC], int& ke) {
+    if (row_ok) {
+      k[0] = lut_key(q.v.x, lb);
+      k[1] = lut_key(q.v.y, lb);
+      k[2] = lut_key(q.v.z, lb);
+      k[3] = lut_key(q.v.w, lb);
+      const int e = lut_key(q.e, lb);
+      ke = slot_ok ? e : trash;
+    } else {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) k[j] = trash;
+      ke = trash;
+    }
+  };
+  RawLut raw[TY + 1];
+  int A[TY + 1][VEC], AE[TY + 1], B[TY + 1][VEC], BE[TY + 1];
+#pragma unroll
+  for (int r = 0; r <= TY; ++r) fetch(raw[r], zs, r);
+#pragma unroll
+  for (int r = 0; r <= TY; ++r) keys(raw[r], ys + r < ny, A[r], AE[r]);
+#pragma unroll
+  for (int r = 0; r <= TY; ++r) fetch(raw[r], zs + 1, r);
+  // one plane step: keys of plane z+1 into Y, fetch of plane z+2, rows of
+  // plane z (X) against plane z+1 (Y); two steps per trip swap X and Y
+  auto step = [&](int (&X)[TY + 1][VEC], int (&XE)[TY + 1], int (&Y)[TY + 1][VEC], int (&YE)[TY + 1],
+                  int64_t z) {
+    const bool zn = z + 1 < nz;
+#pragma unroll
+    for (int r = 0; r <= TY; ++r) keys(raw[r], zn && ys + r < ny, Y[r], YE[r]);
+#pragma unroll
+    for (int r = 0; r <= TY; ++r) fetch(raw[r], z + 2, r);
+    rows3d<1, VEC, C, TY>(X, XE, XE, Y, YE, YE, ys, ny, hist, lofs);
+  };
+  for (int64_t z = zs; z < ze; z += 2) {
+    step(A, AE, B, BE, z);
+    if (z + 1 >= ze) break;
+    step(B, BE, A, AE, z + 1);
+  }
+}
+
 template <int DT, int VEC, int C, int TY>
 __device__ __forceinline__ void tile3d_generic(const typename Elem<DT>::T* grid, int64_t nz, int64_t ny,
                                                int64_t nx, int64_t zs, int64_t ze, int64_t ys, int64_t xb,
@@ -667,12 +817,14 @@ __device__ __forceinline__ void tile3d_generic(const typename Elem<DT>::T* grid,
 template <int DT, int VEC, int C, int TY>
 __global__ __launch_bounds__(kBlock) void hard3d_kernel(HardArgs a, int nbins, int64_t ntx,
                                                         int64_t nty4, int64_t TZ, int64_t ntiles,
-                                                        int vec_ok) {
+                                                        int vec_ok, int nlut) {
   extern __shared__ __align__(16) unsigned char smem[];
   using T = typename Elem<DT>::T;
   BinCtx bc;
   FastBin fb;
-  Lds L = setup_lds<DT, C>(smem, a, nbins, bc, fb);
+  LutBin lb;
+  Lds L = setup_lds<DT, C>(smem, a, nbins, nlut, bc, fb, lb);
+  const bool use_lut = __builtin_amdgcn_readfirstlane(L.flag[1]) != 0;
 
   const T* grid = reinterpret_cast<const T*>(a.grid);
   const int64_t nz = a.nz, ny = a.ny, nx = a.nx;
@@ -691,6 +843,12 @@ __global__ __launch_bounds__(kBlock) void hard3d_kernel(HardArgs a, int nbins, i
     const int64_t zs = tz * TZ;
     const int64_t ze = zs + TZ < nz ? zs + TZ : nz;
     const int64_t xb = tx * CHUNK;
+    if constexpr (DT == 1) {
+      if (use_lut && vok && xb + CHUNK <= nx) {
+        tile3d_lut<VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb);
+        continue;
+      }
+    }
     if (vok && xb + CHUNK <= nx)
       tile3d_fast<DT, VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, fb);
     else
@@ -701,6 +859,34 @@ __global__ __launch_bounds__(kBlock) void hard3d_kernel(HardArgs a, int nbins, i
 }
 
 // ------------------------------------------------------------- launcher
+size_t lds_bytes(int DT, int nbins, int C, int H, int nlut) {
+  size_t a, b, c;
+  return lds_layout(DT, nbins, C, H, nlut, &a, &b, &c);
+}
+
+// Bucket-table entries for H thresholds: two buckets per threshold keep
+// evenly spaced thresholds in distinct buckets.
+int lut_entries(int H) { return 2 * H + 2; }
+
+// Workgroups of `kernel` that fit on one CU with `lds` bytes of LDS each
+// (at most 4: the sweep is issue-bound and more workgroups only add flushes).
+int resident_blocks(const void* kernel, size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, lds) != hipSuccess) n = 1;
+  return n < 1 ? 1 : (n > 4 ? 4 : n);
+}
+
+// Histogram copies of the 3D float kernel: as many as keep three workgroups
+// on a CU (LDS bank conflicts between the lanes of one ds_add cost more than
+// the lost occupancy; measured on 512^3: 16 copies at 3 workgroups per CU beat
+// 8 or 12 copies at 4).
+int copies3d_f32(int nbins, int H) {
+  const size_t budget = 160 * 1024 / 3;
+  for (int c = 32; c > 1; c >>= 1)
+    if (lds_bytes(1, nbins, c, H, lut_entries(H)) <= budget) return c;
+  return 1;
+}
+
 int copies_for(int dt, int nbins) {
   if (dt == 0) return 32;  // uint8: 257 keys, conflict-free layout fits in 33 KB
   const int c = 4500 / (nbins + 1);
@@ -712,31 +898,32 @@ int copies_for(int dt, int nbins) {
   return 1;
 }
 
-size_t lds_bytes(int DT, int nbins, int C, int H) {
-  size_t a, b, c;
-  return lds_layout(DT, nbins, C, H, &a, &b, &c);
-}
-
 template <int DT, int VEC, int C, int TH>
 hipError_t launch2d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInfo& di) {
   constexpr int64_t CHUNK = 64 * VEC;
   const int64_t ntx = (a.nx + CHUNK - 1) / CHUNK;
-  const int64_t nty = (a.ny + TH * kWavesPerBlock - 1) / (TH * kWavesPerBlock);
+  // rows per wave: TH on large grids, fewer when that would leave the chip
+  // short of workgroups (the per-wave row walk is serial)
+  const int64_t want = (int64_t)di.cus * 4;
+  int64_t th = (a.ny * ntx) / (want * kWavesPerBlock);
+  if (th > TH) th = TH;
+  if (th < 1) th = 1;
+  const int64_t nty = (a.ny + th * kWavesPerBlock - 1) / (th * kWavesPerBlock);
   const int64_t ntiles = ntx * nty;
   const size_t esz = DT == 0 ? 1 : 4;
   const int vec_ok = (reinterpret_cast<uintptr_t>(a.grid) % (VEC * esz) == 0) &&
                      ((a.nx * (int64_t)esz) % (int64_t)(VEC * esz) == 0);
-  const size_t lds = lds_bytes(DT, nbins, C, a.H);
-  int64_t g = (int64_t)di.cus * 4;
-  if (g > ntiles) g = ntiles;
-  if (g < 1) g = 1;
+  const size_t lds = lds_bytes(DT, nbins, C, a.H, 0);
   auto k = hard2d_kernel<DT, VEC, C, TH>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), lds, s, a, nbins, ntx, ntiles, vec_ok);
+  int64_t g = (int64_t)di.cus * resident_blocks(reinterpret_cast<const void*>(k), lds);
+  if (g > ntiles) g = ntiles;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), lds, s, a, nbins, ntx, ntiles, vec_ok, (int)th);
   return hipGetLastError();
 }
 
@@ -757,18 +944,20 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   const size_t esz = DT == 0 ? 1 : 4;
   const int vec_ok = (reinterpret_cast<uintptr_t>(a.grid) % (VEC * esz) == 0) &&
                      ((a.nx * (int64_t)esz) % (int64_t)(VEC * esz) == 0);
-  const size_t lds = lds_bytes(DT, nbins, C, a.H);
-  int64_t g = want;
-  if (g > ntiles) g = ntiles;
-  if (g < 1) g = 1;
+  int nlut = (DT == 1 && vec_ok) ? lut_entries(a.H) : 0;
+  if (nlut > 0 && lds_bytes(DT, nbins, C, a.H, nlut) > 128 * 1024) nlut = 0;  // very large H
+  const size_t lds = lds_bytes(DT, nbins, C, a.H, nlut);
   auto k = hard3d_kernel<DT, VEC, C, TY>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
+  int64_t g = (int64_t)di.cus * resident_blocks(reinterpret_cast<const void*>(k), lds);
+  if (g > ntiles) g = ntiles;
+  if (g < 1) g = 1;
   hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), lds, s, a, nbins, ntx, nty4, TZ, ntiles,
-                     vec_ok);
+                     vec_ok, nlut);
   return hipGetLastError();
 }
 
@@ -776,6 +965,10 @@ template <int C>
 hipError_t dispatch_f32(const HardArgs& a, int nbins, hipStream_t s, const DeviceInfo& di) {
   if (a.nz == 1) return launch2d<1, 4, C, 16>(a, nbins, s, di);
   return launch3d<1, 4, C, 4>(a, nbins, s, di);
+}
+
+int copies_f32(const HardArgs& a, int nbins) {
+  return a.nz == 1 ? copies_for(1, nbins) : copies3d_f32(nbins, a.H);
 }
 
 }  // namespace
@@ -789,7 +982,7 @@ hipError_t launch_hard(const HardArgs& a, hipStream_t s) {
     return launch3d<0, 8, 32, 4>(a, 256, s, di);
   }
   const int nbins = a.H;
-  switch (copies_for(1, nbins)) {
+  switch (copies_f32(a, nbins)) {
     case 32: return dispatch_f32<32>(a, nbins, s, di);
     case 16: return dispatch_f32<16>(a, nbins, s, di);
     case 8: return dispatch_f32<8>(a, nbins, s, di);
