@@ -37,13 +37,13 @@ __device__ __forceinline__ void agent_store(double* p, double v) {
 // returns true with the totals in `tot` (LDS, n entries) and leaves the
 // accumulators and the ticket zero for the next launch.  Integer addition is
 // associative, so the totals do not depend on the order of arrival.
-template <typename Local>
+template <int NT = kBlock, typename Local>
 __device__ bool grid_reduce(void* ws, int H, int n, Local local, long long* tot, int* lds_flag) {
   unsigned int* ticket = reinterpret_cast<unsigned int*>(ws);
   long long* acc = reinterpret_cast<long long*>(reinterpret_cast<char*>(ws) + kWsHeader);
   const int stride = acc_bins(H);
   long long* mine = acc + (size_t)(blockIdx.x % kAccCopies) * stride;
-  for (int b = threadIdx.x; b < n; b += kBlock) {
+  for (int b = threadIdx.x; b < n; b += NT) {
     const long long v = local(b);
     if (v != 0) __hip_atomic_fetch_add(mine + b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -57,32 +57,32 @@ __device__ bool grid_reduce(void* ws, int H, int n, Local local, long long* tot,
   }
   __syncthreads();
   if (!*lds_flag) return false;
-  for (int b = threadIdx.x; b < n; b += kBlock) {
+  for (int b = threadIdx.x; b < n; b += NT) {
     long long s = 0;
 #pragma unroll
     for (int c = 0; c < kAccCopies; ++c) s += agent_load(acc + (size_t)c * stride + b);
     tot[b] = s;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kAccCopies * stride; i += kBlock) agent_store(acc + i, 0LL);
+  for (int i = threadIdx.x; i < kAccCopies * stride; i += NT) agent_store(acc + i, 0LL);
   return true;
 }
 
 // --------------------------------------------------------- block scans
-// Inclusive scan of n values with kBlock threads, each thread owning one
+// Inclusive scan of n values with NT threads, each thread owning one
 // contiguous segment.  `get(i)` produces element i (called twice per
-// element), `put(i, v)` receives the inclusive scan.  `tmp` holds kBlock T.
-template <typename T, typename Op, typename Get, typename Put>
+// element), `put(i, v)` receives the inclusive scan.  `tmp` holds NT T.
+template <typename T, int NT = kBlock, typename Op, typename Get, typename Put>
 __device__ void block_scan(int n, T identity, Op op, Get get, Put put, T* tmp) {
   const int t = threadIdx.x;
-  const int seg = (n + kBlock - 1) / kBlock;
+  const int seg = (n + NT - 1) / NT;
   const int b = t * seg;
   const int e = min(b + seg, n);
   T s = identity;
   for (int i = b; i < e; ++i) s = op(s, get(i));
   tmp[t] = s;
   __syncthreads();
-  for (int off = 1; off < kBlock; off <<= 1) {
+  for (int off = 1; off < NT; off <<= 1) {
     T v = t >= off ? tmp[t - off] : identity;
     __syncthreads();
     tmp[t] = op(tmp[t], v);
@@ -99,8 +99,9 @@ __device__ void block_scan(int n, T identity, Op op, Get get, Put put, T* tmp) {
 // Running maximum of the thresholds: R_k = max(tau_0..tau_k) with fmaxf, so a
 // NaN threshold never admits a value.  min{k : v <= tau_k} equals
 // min{k : v <= R_k}, and R is non-decreasing, which makes binning a search.
+template <int NT = kBlock>
 __device__ __forceinline__ void running_max_to_lds(const float* tau, int H, float* R, float* tmp) {
-  block_scan<float>(
+  block_scan<float, NT>(
       H, -__builtin_inff(), [](float a, float b) { return fmaxf(a, b); },
       [&](int i) { return tau[i]; }, [&](int i, float v) { R[i] = v; }, tmp);
 }

@@ -129,7 +129,17 @@ __device__ __forceinline__ int from_right(int v, int edge) {
 // Telescoped weights of one row sequence over this lane's V positions and
 // unconditional histogram updates (an update of 0 costs the same LDS time as
 // a masked one, and needs no exec-mask branches).  sign is +1 or -1.
-template <int V, int C>
+//
+// With ADDR the keys are already the LDS byte addresses of the lane's
+// counters (bin * 4C + 4 * copy + histogram base), so the update needs no
+// address arithmetic.  Comparisons of such keys order different bins
+// correctly (the copy offset is below one bin's stride) and break ties
+// between equal bins arbitrarily, which the telescoped sum allows: an x-edge
+// of two equal keys may go to either end, as long as both ends see the same
+// choice, and they do, because both lanes compare the same two values.
+typedef __attribute__((address_space(3))) int lds_int;
+
+template <int V, int C, bool ADDR = false>
 __device__ __forceinline__ void tele_add(const int (&s)[V], int left, int right, int sign, int* hist,
                                          int lofs) {
   int inc_prev = (int)(s[0] > left);
@@ -139,14 +149,19 @@ __device__ __forceinline__ void tele_add(const int (&s)[V], int left, int right,
     const int inc = (int)(nxt > s[j]);
     const int w = inc - inc_prev;
     inc_prev = inc;
-    atomicAdd(&hist[s[j] * C + lofs], sign > 0 ? w : -w);
+    if constexpr (ADDR)
+      __hip_atomic_fetch_add((lds_int*)(size_t)(unsigned int)s[j], sign > 0 ? w : -w, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+    else
+      atomicAdd(&hist[s[j] * C + lofs], sign > 0 ? w : -w);
   }
 }
 
 // Binning table for float grids: P[k] = (R[k-1], R[k]) with R[-1] = -inf and
 // R[H] = +inf, so v belongs to bin k iff P[k].x < v <= P[k].y.
+template <int NT>
 __device__ __forceinline__ void build_pairs(const float* R, int H, float2* P) {
-  for (int k = threadIdx.x; k <= H; k += kBlock)
+  for (int k = threadIdx.x; k <= H; k += NT)
     P[k] = make_float2(k > 0 ? R[k - 1] : -__builtin_inff(), k < H ? R[k] : __builtin_inff());
 }
 
@@ -177,7 +192,7 @@ __device__ __forceinline__ int bin_fast(float v, const float2* P, const float* R
 // Reduce the workgroup histograms over the grid and let the last workgroup
 // turn the totals into the curve.  `tot`
 // is LDS for nbins int64 that may alias the (no longer needed) histogram.
-template <int DT, int C>
+template <int DT, int C, int NT>
 __device__ __forceinline__ void flush_and_finish(const HardArgs& a, int nbins, int* hist, long long* tmp,
                                                  long long* ch, int* flag, long long* tot) {
   __syncthreads();
@@ -187,16 +202,16 @@ __device__ __forceinline__ void flush_and_finish(const HardArgs& a, int nbins, i
     for (int c = 0; c < C; ++c) s += hist[b * C + c];
     return s;
   };
-  if (!grid_reduce(a.ws, a.H, nbins, local, tot, flag)) return;
+  if (!grid_reduce<NT>(a.ws, a.H, nbins, local, tot, flag)) return;
   int64_t* out = a.out;
   if constexpr (DT == 0) {
     // per-value histogram -> weighted count of values <= v
-    block_scan<long long>(
+    block_scan<long long, NT>(
         256, 0LL, [](long long x, long long y) { return x + y; }, [&](int i) { return tot[i]; },
         [&](int i, long long v) { ch[i] = v; }, tmp);
     // out[k] = weighted count of values <= R_k, R = running max of tau
     float* ftmp = reinterpret_cast<float*>(tmp);
-    block_scan<float>(
+    block_scan<float, NT>(
         a.H, -__builtin_inff(), [](float x, float y) { return fmaxf(x, y); },
         [&](int i) { return a.tau[i]; },
         [&](int i, float r) {
@@ -207,14 +222,14 @@ __device__ __forceinline__ void flush_and_finish(const HardArgs& a, int nbins, i
         },
         ftmp);
   } else {
-    block_scan<long long>(
+    block_scan<long long, NT>(
         a.H, 0LL, [](long long x, long long y) { return x + y; }, [&](int i) { return tot[i]; },
         [&](int i, long long v) { out[i] = v; }, tmp);
   }
 }
 
-template <int DT>
-__device__ __forceinline__ void setup_bins(const HardArgs& a, float* R, long long* tmp, BinCtx& c,
+template <int DT, int NT>
+__device__ __forceinline__ void setup_bins(const HardArgs& a, float* R, float* scan, BinCtx& c,
                                            int nbins) {
   c.H = a.H;
   c.trash = nbins;
@@ -222,7 +237,7 @@ __device__ __forceinline__ void setup_bins(const HardArgs& a, float* R, long lon
   c.r0 = 0.0f;
   c.scale = 0.0f;
   if constexpr (DT == 1) {
-    running_max_to_lds(a.tau, a.H, R, reinterpret_cast<float*>(tmp));
+    running_max_to_lds<NT>(a.tau, a.H, R, scan);
     guess_params(R, a.H, &c.r0, &c.scale);
   }
 }
@@ -464,31 +479,39 @@ __device__ __forceinline__ void tile2d_generic(const typename Elem<DT>::T* grid,
 }
 
 struct Lds {
-  long long* tmp;
-  long long* ch;
-  int* flag;   // [0] last-workgroup flag, [1] bucket table usable
-  int* hist;
+  int* flag;       // [0] last-workgroup flag, [1] bucket table usable
+  int* hist;       // sweep: C interleaved copies of nbins+1 int32 counters
+  float* scan;     // setup: NT scratch values (over the histogram, before it is cleared)
+  long long* tot;  // flush: nbins totals          } over everything after the flag,
+  long long* tmp;  // flush: NT scratch values     } which is dead once the
+  long long* ch;   // uint8 flush: NT value counts } sweep is over
   float* R;
-  float2* P;   // pair table, or
-  float2* lut; // bucket table (same LDS)
+  float2* P;       // pair table, or
+  float2* lut;     // bucket table (same LDS)
 };
 
 __host__ __device__ inline size_t align16(size_t b) { return (b + 15) & ~(size_t)15; }
 
-// LDS: [tmp | ch | flag] (fixed, so the histogram sits at a compile-time
-// offset that folds into every ds_add) | histogram | R | X, where X holds
-// either the bucket table (nlut entries) or, when there is none or it cannot
-// be used, the pair table P (H+1 entries).
-__host__ __device__ inline size_t lds_layout(int DT, int nbins, int C, int H, int nlut, size_t* off_hist,
+// LDS: flag (16 bytes, so the histogram sits at a compile-time offset that
+// folds into every ds_add) | histogram | R | X.  X holds either the bucket
+// table (nlut entries) or, when there is none or it cannot be used, the pair
+// table P (H+1 entries).  Setup scratch overlays the histogram before it is
+// cleared; the flush's totals and scratch overlay everything after the flag.
+__host__ __device__ inline size_t lds_flush_offset(int nbins) {
+  return 16 + align16((size_t)nbins * sizeof(long long));
+}
+
+__host__ __device__ inline size_t lds_layout(int DT, int nbins, int C, int H, int nlut, int NT,
                                              size_t* off_R, size_t* off_X) {
-  size_t b = 2 * kBlock * sizeof(long long) + 4 * sizeof(int);
-  *off_hist = b;
-  b = align16(b + (size_t)(nbins + 1) * C * sizeof(int));
+  size_t hist = (size_t)(nbins + 1) * C * sizeof(int);
+  if (hist < (size_t)NT * sizeof(long long)) hist = (size_t)NT * sizeof(long long);
+  size_t b = 16 + align16(hist);
   *off_R = b;
   if (DT == 1) b = align16(b + (size_t)H * sizeof(float));
   *off_X = b;
   if (DT == 1) b += (size_t)(nlut > H + 1 ? nlut : H + 1) * sizeof(float2);
-  return b;
+  const size_t flush = lds_flush_offset(nbins) + 2 * (size_t)NT * sizeof(long long);
+  return b > flush ? b : flush;
 }
 
 // ------------------------------------------------------------ bucket table
@@ -504,21 +527,24 @@ __host__ __device__ inline size_t lds_layout(int DT, int nbins, int C, int H, in
 // one-per-bucket condition (with finite, increasing end points), otherwise
 // the sweep takes the checked path.
 struct LutBin {
-  const float2* lut;  // (thr, base as int bits)
+  const float2* lut;  // (thr, LDS byte address of bin base's counters, as int bits)
   float mul, add, hi;
+  int lo4, hi4;       // this lane's copy offset in bytes, and that plus one bin's stride
 };
 
 __device__ __forceinline__ int lut_bucket(float v, const LutBin& lb) {
   return (int)__builtin_amdgcn_fmed3f(fmaf(v, lb.mul, lb.add), 0.0f, lb.hi);
 }
 
+// Key of v: the LDS byte address of this lane's counter for bin(v).
 __device__ __forceinline__ int lut_key(float v, const LutBin& lb) {
   const float2 e = lb.lut[lut_bucket(v, lb)];
-  return __float_as_int(e.y) + (int)(v > e.x);
+  return __float_as_int(e.y) + ((v > e.x) ? lb.hi4 : lb.lo4);
 }
 
+template <int NT>
 __device__ __forceinline__ void build_lut(const float* R, int H, int n, float2* lut, int* ok_flag,
-                                          LutBin& lb) {
+                                          LutBin& lb, unsigned int hist_addr, unsigned int stride) {
   const float lo = R[0], hi = R[H - 1];
   const float INF = __builtin_inff();
   float mul = 0.0f, add = 0.0f;
@@ -537,34 +563,36 @@ __device__ __forceinline__ void build_lut(const float* R, int H, int n, float2* 
   __syncthreads();
   if (!*ok_flag) return;  // uniform: every thread read the same flag
   bool mine = true;
-  for (int k = threadIdx.x; k <= H; k += kBlock) {
+  for (int k = threadIdx.x; k <= H; k += NT) {
     const int bprev = k > 0 ? lut_bucket(R[k - 1], lb) : -1;
     const int bk = k < H ? lut_bucket(R[k], lb) : n - 1;
     if (k > 0 && k < H && bk <= bprev) mine = false;
     for (int j = bprev + 1; j <= bk; ++j)
-      lut[j] = make_float2((k < H && j == bk) ? R[k] : INF, __int_as_float(k));
+      lut[j] = make_float2((k < H && j == bk) ? R[k] : INF, __int_as_float((int)(hist_addr + stride * (unsigned int)k)));
   }
   __syncthreads();
   if (!mine) *ok_flag = 0;  // benign race: every writer stores 0
   __syncthreads();
 }
 
-template <int DT, int C>
+template <int DT, int C, int NT>
 __device__ __forceinline__ Lds setup_lds(unsigned char* smem, const HardArgs& a, int nbins, int nlut,
                                          BinCtx& bc, FastBin& fb, LutBin& lb) {
-  size_t oh, oR, oX;
-  lds_layout(DT, nbins, C, a.H, nlut, &oh, &oR, &oX);
+  size_t oR, oX;
+  lds_layout(DT, nbins, C, a.H, nlut, NT, &oR, &oX);
   Lds L;
-  L.tmp = reinterpret_cast<long long*>(smem);
-  L.ch = L.tmp + kBlock;
-  L.flag = reinterpret_cast<int*>(L.ch + kBlock);
-  L.hist = reinterpret_cast<int*>(smem + oh);
+  L.flag = reinterpret_cast<int*>(smem);
+  L.hist = reinterpret_cast<int*>(smem + 16);
+  L.scan = reinterpret_cast<float*>(smem + 16);
+  L.tot = reinterpret_cast<long long*>(smem + 16);
+  L.tmp = reinterpret_cast<long long*>(smem + lds_flush_offset(nbins));
+  L.ch = L.tmp + NT;
   L.R = reinterpret_cast<float*>(smem + oR);
   L.P = reinterpret_cast<float2*>(smem + oX);
   L.lut = reinterpret_cast<float2*>(smem + oX);
-  for (int i = threadIdx.x; i < (nbins + 1) * C; i += kBlock) L.hist[i] = 0;
   if (threadIdx.x == 0) L.flag[1] = 0;
-  setup_bins<DT>(a, L.R, L.tmp, bc, nbins);
+  setup_bins<DT, NT>(a, L.R, L.scan, bc, nbins);  // ends with a barrier
+  for (int i = threadIdx.x; i < (nbins + 1) * C; i += NT) L.hist[i] = 0;
   fb.P = L.P;
   fb.R = L.R;
   fb.H = a.H;
@@ -573,25 +601,29 @@ __device__ __forceinline__ Lds setup_lds(unsigned char* smem, const HardArgs& a,
   if (!(fb.add > -__builtin_inff() && fb.add < __builtin_inff())) { fb.mul = 0.0f; fb.add = 0.0f; }
   lb.lut = L.lut;
   lb.mul = lb.add = lb.hi = 0.0f;
+  lb.lo4 = 4 * ((threadIdx.x & 63) & (C - 1));
+  lb.hi4 = lb.lo4 + 4 * C;
   __syncthreads();
   if constexpr (DT == 1) {
-    if (nlut > 0) build_lut(L.R, a.H, nlut, L.lut, L.flag + 1, lb);
+    if (nlut > 0)
+      build_lut<NT>(L.R, a.H, nlut, L.lut, L.flag + 1, lb, (unsigned int)(size_t)(lds_int*)L.hist,
+                    4u * (unsigned int)C);
     // the pair table is only needed when the bucket table is not used
-    if (!L.flag[1]) build_pairs(L.R, a.H, L.P);
+    if (!L.flag[1]) build_pairs<NT>(L.R, a.H, L.P);
   }
   __syncthreads();
   return L;
 }
 
-template <int DT, int VEC, int C, int TH>
-__global__ __launch_bounds__(kBlock) void hard2d_kernel(HardArgs a, int nbins, int64_t ntx,
-                                                        int64_t ntiles, int vec_ok, int th) {
+template <int DT, int VEC, int C, int TH, int NT>
+__global__ __launch_bounds__(NT) void hard2d_kernel(HardArgs a, int nbins, int64_t ntx, int64_t ntiles,
+                                                    int vec_ok, int th) {
   extern __shared__ __align__(16) unsigned char smem[];
   using T = typename Elem<DT>::T;
   BinCtx bc;
   FastBin fb;
   LutBin lb;
-  Lds L = setup_lds<DT, C>(smem, a, nbins, 0, bc, fb, lb);
+  Lds L = setup_lds<DT, C, NT>(smem, a, nbins, 0, bc, fb, lb);
 
   const T* grid = reinterpret_cast<const T*>(a.grid);
   const int64_t ny = a.ny, nx = a.nx;
@@ -603,7 +635,7 @@ __global__ __launch_bounds__(kBlock) void hard2d_kernel(HardArgs a, int nbins, i
 
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t tx = t % ntx, tyb = t / ntx;
-    const int64_t ys = (tyb * kWavesPerBlock + wave) * th;
+    const int64_t ys = (tyb * (NT / 64) + wave) * th;
     if (ys >= ny) continue;
     const int64_t ye = ys + th < ny ? ys + th : ny;
     const int64_t xb = tx * CHUNK;
@@ -612,8 +644,7 @@ __global__ __launch_bounds__(kBlock) void hard2d_kernel(HardArgs a, int nbins, i
     else
       tile2d_generic<DT, VEC, C>(grid, ny, nx, ys, ye, xb, lane, lofs, L.hist, vok, bc);
   }
-  long long* tot = C >= 2 ? reinterpret_cast<long long*>(L.hist) : reinterpret_cast<long long*>(L.R);
-  flush_and_finish<DT, C>(a, nbins, L.hist, L.tmp, L.ch, L.flag, tot);
+  flush_and_finish<DT, C, NT>(a, nbins, L.hist, L.tmp, L.ch, L.flag, L.tot);
 }
 
 // ------------------------------------------------------------------- 3D
@@ -621,7 +652,7 @@ __global__ __launch_bounds__(kBlock) void hard2d_kernel(HardArgs a, int nbins, i
 // wave marches along z holding the keys of TY+1 rows (TY plus a one-row
 // halo) of planes z and z+1; the raw rows of plane z+2 are in flight while
 // plane z is processed.
-template <int DT, int VEC, int C, int TY>
+template <int DT, int VEC, int C, int TY, bool ADDR = false>
 __device__ __forceinline__ void rows3d(int (&A)[TY + 1][VEC], int (&AL)[TY + 1], int (&AR)[TY + 1],
                                        int (&B)[TY + 1][VEC], int (&BL)[TY + 1], int (&BR)[TY + 1],
                                        int64_t ys, int64_t ny, int* hist, int lofs) {
@@ -637,10 +668,10 @@ __device__ __forceinline__ void rows3d(int (&A)[TY + 1][VEC], int (&AL)[TY + 1],
       }
       const int e2l = max(AL[r], AL[r + 1]), e3l = max(AL[r], BL[r]), e4l = max(e2l, max(BL[r], BL[r + 1]));
       const int e2r = max(AR[r], AR[r + 1]), e3r = max(AR[r], BR[r]), e4r = max(e2r, max(BR[r], BR[r + 1]));
-      tele_add<VEC, C>(A[r], from_left(A[r][VEC - 1], AL[r]), from_right(A[r][0], AR[r]), 1, hist, lofs);
-      tele_add<VEC, C>(s2, from_left(s2[VEC - 1], e2l), from_right(s2[0], e2r), -1, hist, lofs);
-      tele_add<VEC, C>(s3, from_left(s3[VEC - 1], e3l), from_right(s3[0], e3r), -1, hist, lofs);
-      tele_add<VEC, C>(s4, from_left(s4[VEC - 1], e4l), from_right(s4[0], e4r), 1, hist, lofs);
+      tele_add<VEC, C, ADDR>(A[r], from_left(A[r][VEC - 1], AL[r]), from_right(A[r][0], AR[r]), 1, hist, lofs);
+      tele_add<VEC, C, ADDR>(s2, from_left(s2[VEC - 1], e2l), from_right(s2[0], e2r), -1, hist, lofs);
+      tele_add<VEC, C, ADDR>(s3, from_left(s3[VEC - 1], e3l), from_right(s3[0], e3r), -1, hist, lofs);
+      tele_add<VEC, C, ADDR>(s4, from_left(s4[VEC - 1], e4l), from_right(s4[0], e4r), 1, hist, lofs);
     }
   }
 }
@@ -717,16 +748,18 @@ struct RawLut {
 template <int VEC, int C, int TY>
 __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_t ny, int64_t nx, int64_t zs,
                                            int64_t ze, int64_t ys, int64_t xb, int lane, int lofs, int* hist,
-                                           int trash, const LutBin& lb) {
+                                           int trash_bin, const LutBin& lb) {
   static_assert(VEC == 4, "float rows are loaded as float4");
+  // keys are LDS byte addresses of this lane's counters (see tele_add)
+  const int trash = (int)((unsigned int)(size_t)(lds_int*)hist + 4u * (unsigned int)(C * trash_bin)) + lb.lo4;
   constexpr int64_t CHUNK = 64 * VEC;
   const int64_t plane = ny * nx;
   const bool has_l = xb > 0, has_r = xb + CHUNK < nx;
   const bool lane0 = lane == 0;
   const bool slot_ok = lane0 ? has_l : has_r;
   // byte offsets from the element just left of the chunk: vector at 4 + 16 lane,
-  // edge at 0 (left) or 4 (CHUNK + 1) (right); a missing edge reads the chunk's
-  // first element instead (its key is replaced by trash)
+  // edge at 0 (left) or 4 (CHUNK + 1) (right); a missing edge reads the
+  // chunk's first element instead (its key is replaced by trash)
   const unsigned int voff = 4u + 16u * (unsigned int)lane;
   const unsigned int eoff = lane0 ? (has_l ? 0u : 4u) : (has_r ? 4u * (unsigned int)(CHUNK + 1) : 4u);
   int64_t roff[TY + 1];
@@ -768,7 +801,7 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
     for (int r = 0; r <= TY; ++r) keys(raw[r], zn && ys + r < ny, Y[r], YE[r]);
 #pragma unroll
     for (int r = 0; r <= TY; ++r) fetch(raw[r], z + 2, r);
-    rows3d<1, VEC, C, TY>(X, XE, XE, Y, YE, YE, ys, ny, hist, lofs);
+    rows3d<1, VEC, C, TY, true>(X, XE, XE, Y, YE, YE, ys, ny, hist, lofs);
   };
   for (int64_t z = zs; z < ze; z += 2) {
     step(A, AE, B, BE, z);
@@ -814,16 +847,18 @@ __device__ __forceinline__ void tile3d_generic(const typename Elem<DT>::T* grid,
   }
 }
 
-template <int DT, int VEC, int C, int TY>
-__global__ __launch_bounds__(kBlock) void hard3d_kernel(HardArgs a, int nbins, int64_t ntx,
-                                                        int64_t nty4, int64_t TZ, int64_t ntiles,
-                                                        int vec_ok, int nlut) {
+// NT threads per workgroup; MINW waves per SIMD that the register budget must
+// allow (so that two 512-thread workgroups share a CU).
+template <int DT, int VEC, int C, int TY, int NT, int MINW>
+__global__ __launch_bounds__(NT, MINW) void hard3d_kernel(HardArgs a, int nbins, int64_t ntx,
+                                                          int64_t nty4, int64_t TZ, int64_t ntiles,
+                                                          int vec_ok, int nlut) {
   extern __shared__ __align__(16) unsigned char smem[];
   using T = typename Elem<DT>::T;
   BinCtx bc;
   FastBin fb;
   LutBin lb;
-  Lds L = setup_lds<DT, C>(smem, a, nbins, nlut, bc, fb, lb);
+  Lds L = setup_lds<DT, C, NT>(smem, a, nbins, nlut, bc, fb, lb);
   const bool use_lut = __builtin_amdgcn_readfirstlane(L.flag[1]) != 0;
 
   const T* grid = reinterpret_cast<const T*>(a.grid);
@@ -838,7 +873,7 @@ __global__ __launch_bounds__(kBlock) void hard3d_kernel(HardArgs a, int nbins, i
     const int64_t tx = t % ntx;
     const int64_t rest = t / ntx;
     const int64_t tyg = rest % nty4, tz = rest / nty4;
-    const int64_t ys = (tyg * kWavesPerBlock + wave) * TY;
+    const int64_t ys = (tyg * (NT / 64) + wave) * TY;
     if (ys >= ny) continue;
     const int64_t zs = tz * TZ;
     const int64_t ze = zs + TZ < nz ? zs + TZ : nz;
@@ -854,14 +889,13 @@ __global__ __launch_bounds__(kBlock) void hard3d_kernel(HardArgs a, int nbins, i
     else
       tile3d_generic<DT, VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lofs, L.hist, vok, bc, lane);
   }
-  long long* tot = C >= 2 ? reinterpret_cast<long long*>(L.hist) : reinterpret_cast<long long*>(L.R);
-  flush_and_finish<DT, C>(a, nbins, L.hist, L.tmp, L.ch, L.flag, tot);
+  flush_and_finish<DT, C, NT>(a, nbins, L.hist, L.tmp, L.ch, L.flag, L.tot);
 }
 
 // ------------------------------------------------------------- launcher
-size_t lds_bytes(int DT, int nbins, int C, int H, int nlut) {
-  size_t a, b, c;
-  return lds_layout(DT, nbins, C, H, nlut, &a, &b, &c);
+size_t lds_bytes(int DT, int nbins, int C, int H, int nlut, int NT) {
+  size_t a, b;
+  return lds_layout(DT, nbins, C, H, nlut, NT, &a, &b);
 }
 
 // Bucket-table entries for H thresholds: two buckets per threshold keep
@@ -870,20 +904,24 @@ int lut_entries(int H) { return 2 * H + 2; }
 
 // Workgroups of `kernel` that fit on one CU with `lds` bytes of LDS each
 // (at most 4: the sweep is issue-bound and more workgroups only add flushes).
-int resident_blocks(const void* kernel, size_t lds) {
+int resident_blocks(const void* kernel, int nt, size_t lds) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, lds) != hipSuccess) n = 1;
-  return n < 1 ? 1 : (n > 4 ? 4 : n);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, nt, lds) != hipSuccess) n = 1;
+  const int cap = 4 * 256 / nt;
+  return n < 1 ? 1 : (n > cap ? cap : n);
 }
 
-// Histogram copies of the 3D float kernel: as many as keep three workgroups
-// on a CU (LDS bank conflicts between the lanes of one ds_add cost more than
-// the lost occupancy; measured on 512^3: 16 copies at 3 workgroups per CU beat
-// 8 or 12 copies at 4).
+// Threads per workgroup of the 3D float kernel.
+constexpr int kNT3 = 512;
+
+// Histogram copies of the 3D float kernel: as many as keep two 512-thread
+// workgroups on a CU.  LDS serves a ds_add 32 lanes at a time; with 32
+// copies interleaved by lane those lanes always hit distinct banks, with
+// fewer copies random keys collide and the instruction takes several passes.
 int copies3d_f32(int nbins, int H) {
-  const size_t budget = 160 * 1024 / 3;
+  const size_t budget = 160 * 1024 / 2;
   for (int c = 32; c > 1; c >>= 1)
-    if (lds_bytes(1, nbins, c, H, lut_entries(H)) <= budget) return c;
+    if (lds_bytes(1, nbins, c, H, lut_entries(H), kNT3) <= budget) return c;
   return 1;
 }
 
@@ -913,27 +951,28 @@ hipError_t launch2d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   const size_t esz = DT == 0 ? 1 : 4;
   const int vec_ok = (reinterpret_cast<uintptr_t>(a.grid) % (VEC * esz) == 0) &&
                      ((a.nx * (int64_t)esz) % (int64_t)(VEC * esz) == 0);
-  const size_t lds = lds_bytes(DT, nbins, C, a.H, 0);
-  auto k = hard2d_kernel<DT, VEC, C, TH>;
+  const size_t lds = lds_bytes(DT, nbins, C, a.H, 0, kBlock);
+  auto k = hard2d_kernel<DT, VEC, C, TH, kBlock>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  int64_t g = (int64_t)di.cus * resident_blocks(reinterpret_cast<const void*>(k), lds);
+  int64_t g = (int64_t)di.cus * resident_blocks(reinterpret_cast<const void*>(k), kBlock, lds);
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
   hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), lds, s, a, nbins, ntx, ntiles, vec_ok, (int)th);
   return hipGetLastError();
 }
 
-template <int DT, int VEC, int C, int TY>
+template <int DT, int VEC, int C, int TY, int NT, int MINW>
 hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInfo& di) {
   constexpr int64_t CHUNK = 64 * VEC;
+  constexpr int64_t WAVES = NT / 64;
   const int64_t ntx = (a.nx + CHUNK - 1) / CHUNK;
-  const int64_t nty4 = (a.ny + TY * kWavesPerBlock - 1) / (TY * kWavesPerBlock);
+  const int64_t nty4 = (a.ny + TY * WAVES - 1) / (TY * WAVES);
   // split z so that there are enough tiles to fill the chip
-  const int64_t want = (int64_t)di.cus * 4;
+  const int64_t want = (int64_t)di.cus * (4 * 256 / NT);
   int64_t ntz = (want + ntx * nty4 - 1) / (ntx * nty4);
   if (ntz < 1) ntz = 1;
   if (ntz > a.nz) ntz = a.nz;
@@ -945,18 +984,18 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   const int vec_ok = (reinterpret_cast<uintptr_t>(a.grid) % (VEC * esz) == 0) &&
                      ((a.nx * (int64_t)esz) % (int64_t)(VEC * esz) == 0);
   int nlut = (DT == 1 && vec_ok) ? lut_entries(a.H) : 0;
-  if (nlut > 0 && lds_bytes(DT, nbins, C, a.H, nlut) > 128 * 1024) nlut = 0;  // very large H
-  const size_t lds = lds_bytes(DT, nbins, C, a.H, nlut);
-  auto k = hard3d_kernel<DT, VEC, C, TY>;
+  if (nlut > 0 && lds_bytes(DT, nbins, C, a.H, nlut, NT) > 128 * 1024) nlut = 0;  // very large H
+  const size_t lds = lds_bytes(DT, nbins, C, a.H, nlut, NT);
+  auto k = hard3d_kernel<DT, VEC, C, TY, NT, MINW>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  int64_t g = (int64_t)di.cus * resident_blocks(reinterpret_cast<const void*>(k), lds);
+  int64_t g = (int64_t)di.cus * resident_blocks(reinterpret_cast<const void*>(k), NT, lds);
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
-  hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), lds, s, a, nbins, ntx, nty4, TZ, ntiles,
+  hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(NT), lds, s, a, nbins, ntx, nty4, TZ, ntiles,
                      vec_ok, nlut);
   return hipGetLastError();
 }
@@ -964,7 +1003,7 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
 template <int C>
 hipError_t dispatch_f32(const HardArgs& a, int nbins, hipStream_t s, const DeviceInfo& di) {
   if (a.nz == 1) return launch2d<1, 4, C, 16>(a, nbins, s, di);
-  return launch3d<1, 4, C, 4>(a, nbins, s, di);
+  return launch3d<1, 4, C, 4, kNT3, 4>(a, nbins, s, di);
 }
 
 int copies_f32(const HardArgs& a, int nbins) {
@@ -979,7 +1018,7 @@ hipError_t launch_hard(const HardArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (a.dtype == 0) {
     if (a.nz == 1) return launch2d<0, 16, 32, 16>(a, 256, s, di);
-    return launch3d<0, 8, 32, 4>(a, 256, s, di);
+    return launch3d<0, 8, 32, 4, kBlock, 1>(a, 256, s, di);
   }
   const int nbins = a.H;
   switch (copies_f32(a, nbins)) {
