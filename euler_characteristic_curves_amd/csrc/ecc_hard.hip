@@ -30,6 +30,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <type_traits>
+
 #include "ecc_device.hpp"
 #include "ecc_internal.hpp"
 
@@ -373,15 +376,15 @@ __device__ __forceinline__ void row_keys(const RawRow<DT, VEC>& raw, bool valid,
 // One row step: cur/nxt keys of rows y and y+1 (lane-local), edge keys from
 // outside the chunk; two telescoped sequences (the row and the max of the two
 // rows) go to the histogram.
-template <int VEC, int C>
+template <int VEC, int C, bool ADDR = false>
 __device__ __forceinline__ void row2d(const int (&cur)[VEC], int cl, int cr, const int (&nxt)[VEC], int nl,
                                       int nr, int* hist, int lofs) {
   int s2[VEC];
 #pragma unroll
   for (int j = 0; j < VEC; ++j) s2[j] = max(cur[j], nxt[j]);
-  tele_add<VEC, C>(cur, from_left(cur[VEC - 1], cl), from_right(cur[0], cr), 1, hist, lofs);
-  tele_add<VEC, C>(s2, from_left(s2[VEC - 1], max(cl, nl)), from_right(s2[0], max(cr, nr)), -1, hist,
-                   lofs);
+  tele_add<VEC, C, ADDR>(cur, from_left(cur[VEC - 1], cl), from_right(cur[0], cr), 1, hist, lofs);
+  tele_add<VEC, C, ADDR>(s2, from_left(s2[VEC - 1], max(cl, nl)), from_right(s2[0], max(cr, nr)), -1,
+                         hist, lofs);
 }
 
 // Interior wave tile (aligned rows, column chunk inside the grid).  Rows
@@ -396,6 +399,18 @@ __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, in
                                             int* hist, int trash, const FastBin& fb) {
   using T = typename Elem<DT>::T;
   constexpr int64_t CHUNK = 64 * VEC;
+  // uint8 grids carry keys as LDS counter addresses (see tele_add): one
+  // shift-add per value instead of one per histogram update
+  constexpr bool ADDR = DT == 0;
+  const unsigned int abase = (unsigned int)(size_t)(lds_int*)hist + 4u * (unsigned int)lofs;
+  auto to_addr = [&](int (&k)[VEC], int& kl, int& kr) {
+    if constexpr (ADDR) {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) k[j] = (int)(abase + 4u * C * (unsigned int)k[j]);
+      kl = (int)(abase + 4u * C * (unsigned int)kl);
+      kr = (int)(abase + 4u * C * (unsigned int)kr);
+    }
+  };
   const bool has_l = xb > 0, has_r = xb + CHUNK < nx;
   const int64_t xl = has_l ? xb - 1 : xb, xr = has_r ? xb + CHUNK : xb;
   const T* lastrow = grid + (ny - 1) * nx;
@@ -410,6 +425,7 @@ __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, in
     fetch_row<DT, VEC>(q2, rowp(ys + 3), xb, lane, xl, xr);
     fetch_row<DT, VEC>(q3, rowp(ys + 4), xb, lane, xl, xr);
     row_keys<DT, VEC>(r0, true, has_l, has_r, trash, fb, cur, cl, cr);
+    to_addr(cur, cl, cr);
   }
   int nxt[VEC], nl, nr;
   // main loop: four rows per trip, every "next" row inside the grid, one load per
@@ -417,8 +433,9 @@ __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, in
 #define ECC_ROW2D_FAST(Q, K)                                                         \
   {                                                                                  \
     row_keys<DT, VEC, false>(Q, true, has_l, has_r, trash, fb, nxt, nl, nr);         \
+    to_addr(nxt, nl, nr);                                                            \
     fetch_row<DT, VEC>(Q, rowp(y + K + 5), xb, lane, xl, xr);                        \
-    row2d<VEC, C>(cur, cl, cr, nxt, nl, nr, hist, lofs);                             \
+    row2d<VEC, C, ADDR>(cur, cl, cr, nxt, nl, nr, hist, lofs);                       \
     _Pragma("unroll") for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];                 \
     cl = nl;                                                                         \
     cr = nr;                                                                         \
@@ -427,7 +444,8 @@ __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, in
 #define ECC_ROW2D_TAIL(Q, K)                                                         \
   if (y + K < ye) {                                                                  \
     row_keys<DT, VEC, true>(Q, y + K + 1 < ny, has_l, has_r, trash, fb, nxt, nl, nr); \
-    row2d<VEC, C>(cur, cl, cr, nxt, nl, nr, hist, lofs);                             \
+    to_addr(nxt, nl, nr);                                                            \
+    row2d<VEC, C, ADDR>(cur, cl, cr, nxt, nl, nr, hist, lofs);                       \
     _Pragma("unroll") for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];                 \
     cl = nl;                                                                         \
     cr = nr;                                                                         \
@@ -633,17 +651,26 @@ __global__ __launch_bounds__(NT) void hard2d_kernel(HardArgs a, int nbins, int64
   constexpr int64_t CHUNK = 64 * VEC;
   const bool vok = vec_ok != 0;
 
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t tx = t % ntx, tyb = t / ntx;
-    const int64_t ys = (tyb * (NT / 64) + wave) * th;
-    if (ys >= ny) continue;
-    const int64_t ye = ys + th < ny ? ys + th : ny;
-    const int64_t xb = tx * CHUNK;
-    if (vok && xb + CHUNK <= nx)
-      tile2d_fast<DT, VEC, C>(grid, ny, nx, ys, ye, xb, lane, lofs, L.hist, nbins, fb);
-    else
-      tile2d_generic<DT, VEC, C>(grid, ny, nx, ys, ye, xb, lane, lofs, L.hist, vok, bc);
-  }
+  // th == TH (large grids) keeps the tile height a compile-time constant,
+  // which lets the compiler schedule the unrolled row loop as a whole
+  auto sweep = [&](auto thc) {
+    const int64_t h = thc.value > 0 ? (int64_t)thc.value : (int64_t)th;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+      const int64_t tx = t % ntx, tyb = t / ntx;
+      const int64_t ys = (tyb * (NT / 64) + wave) * h;
+      if (ys >= ny) continue;
+      const int64_t ye = ys + h < ny ? ys + h : ny;
+      const int64_t xb = tx * CHUNK;
+      if (vok && xb + CHUNK <= nx)
+        tile2d_fast<DT, VEC, C>(grid, ny, nx, ys, ye, xb, lane, lofs, L.hist, nbins, fb);
+      else
+        tile2d_generic<DT, VEC, C>(grid, ny, nx, ys, ye, xb, lane, lofs, L.hist, vok, bc);
+    }
+  };
+  if (th == TH)
+    sweep(std::integral_constant<int, TH>{});
+  else
+    sweep(std::integral_constant<int, 0>{});
   flush_and_finish<DT, C, NT>(a, nbins, L.hist, L.tmp, L.ch, L.flag, L.tot);
 }
 
@@ -904,11 +931,44 @@ int lut_entries(int H) { return 2 * H + 2; }
 
 // Workgroups of `kernel` that fit on one CU with `lds` bytes of LDS each
 // (at most 4: the sweep is issue-bound and more workgroups only add flushes).
+// Raise a kernel's dynamic-LDS limit to the whole CU once (the default is
+// 64 KB); later calls cost a lookup.
+hipError_t allow_lds(const void* kernel, size_t lds) {
+  if (lds <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  struct Entry { const void* k; int dev; };
+  static std::mutex mu;
+  static Entry done[64];
+  static int used = 0;
+  std::lock_guard<std::mutex> g(mu);
+  for (int i = 0; i < used; ++i)
+    if (done[i].k == kernel && done[i].dev == dev) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess && used < 64) done[used++] = Entry{kernel, dev};
+  return e;
+}
+
+// The answer is cached per (kernel, LDS size): the query costs more host
+// time than a small launch takes on the GPU.
 int resident_blocks(const void* kernel, int nt, size_t lds) {
+  struct Entry { const void* k; size_t lds; int n; };
+  static std::mutex mu;
+  static Entry cache[64];
+  static int used = 0;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    for (int i = 0; i < used; ++i)
+      if (cache[i].k == kernel && cache[i].lds == lds) return cache[i].n;
+  }
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, nt, lds) != hipSuccess) n = 1;
   const int cap = 4 * 256 / nt;
-  return n < 1 ? 1 : (n > cap ? cap : n);
+  n = n < 1 ? 1 : (n > cap ? cap : n);
+  std::lock_guard<std::mutex> g(mu);
+  if (used < 64) cache[used++] = Entry{kernel, lds, n};
+  return n;
 }
 
 // Threads per workgroup of the 3D float kernel.
@@ -953,9 +1013,8 @@ hipError_t launch2d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
                      ((a.nx * (int64_t)esz) % (int64_t)(VEC * esz) == 0);
   const size_t lds = lds_bytes(DT, nbins, C, a.H, 0, kBlock);
   auto k = hard2d_kernel<DT, VEC, C, TH, kBlock>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds);
     if (e != hipSuccess) return e;
   }
   int64_t g = (int64_t)di.cus * resident_blocks(reinterpret_cast<const void*>(k), kBlock, lds);
@@ -987,9 +1046,8 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   if (nlut > 0 && lds_bytes(DT, nbins, C, a.H, nlut, NT) > 128 * 1024) nlut = 0;  // very large H
   const size_t lds = lds_bytes(DT, nbins, C, a.H, nlut, NT);
   auto k = hard3d_kernel<DT, VEC, C, TY, NT, MINW>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(k), lds);
     if (e != hipSuccess) return e;
   }
   int64_t g = (int64_t)di.cus * resident_blocks(reinterpret_cast<const void*>(k), NT, lds);
