@@ -772,7 +772,10 @@ struct RawLut {
   float e;
 };
 
-template <int VEC, int C, int TY>
+// SCALAR: element loads with the column clamped to the grid, and trash keys
+// for columns past its end, for a chunk that sticks out of the grid or rows
+// that are not 16-byte aligned.
+template <int VEC, int C, int TY, bool SCALAR>
 __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_t ny, int64_t nx, int64_t zs,
                                            int64_t ze, int64_t ys, int64_t xb, int lane, int lofs, int* hist,
                                            int trash_bin, const LutBin& lb) {
@@ -792,9 +795,27 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
   int64_t roff[TY + 1];
 #pragma unroll
   for (int r = 0; r <= TY; ++r) roff[r] = uni64((ys + r < ny ? ys + r : ny - 1) * nx + xb - 1);
+  // SCALAR: last valid column relative to the chunk start, and this lane's
+  // four clamped byte offsets
+  const int lim = (int)(nx - 1 - xb < CHUNK ? nx - 1 - xb : CHUNK - 1);
+  unsigned int coff[VEC];
+  bool cok[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    const int col = 4 * lane + j;
+    cok[j] = col <= lim;
+    coff[j] = 4u + 4u * (unsigned int)(col <= lim ? col : lim);
+  }
   auto fetch = [&](RawLut& q, int64_t z, int r) {
     const char* base = reinterpret_cast<const char*>(grid + uni64((z < nz ? z : nz - 1) * plane + roff[r]));
-    q.v = *reinterpret_cast<const float4*>(base + voff);
+    if constexpr (SCALAR) {
+      q.v.x = *reinterpret_cast<const float*>(base + coff[0]);
+      q.v.y = *reinterpret_cast<const float*>(base + coff[1]);
+      q.v.z = *reinterpret_cast<const float*>(base + coff[2]);
+      q.v.w = *reinterpret_cast<const float*>(base + coff[3]);
+    } else {
+      q.v = *reinterpret_cast<const float4*>(base + voff);
+    }
     q.e = *reinterpret_cast<const float*>(base + eoff);
   };
   auto keys = [&](const RawLut& q, bool row_ok, int (&k)[VEC], int& ke) {
@@ -803,6 +824,10 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
       k[1] = lut_key(q.v.y, lb);
       k[2] = lut_key(q.v.z, lb);
       k[3] = lut_key(q.v.w, lb);
+      if constexpr (SCALAR) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) k[j] = cok[j] ? k[j] : trash;
+      }
       const int e = lut_key(q.e, lb);
       ke = slot_ok ? e : trash;
     } else {
@@ -906,8 +931,11 @@ __global__ __launch_bounds__(NT, MINW) void hard3d_kernel(HardArgs a, int nbins,
     const int64_t ze = zs + TZ < nz ? zs + TZ : nz;
     const int64_t xb = tx * CHUNK;
     if constexpr (DT == 1) {
-      if (use_lut && vok && xb + CHUNK <= nx) {
-        tile3d_lut<VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb);
+      if (use_lut) {
+        if (vok && xb + CHUNK <= nx)
+          tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb);
+        else
+          tile3d_lut<VEC, C, TY, true>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb);
         continue;
       }
     }
@@ -1042,7 +1070,7 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   const size_t esz = DT == 0 ? 1 : 4;
   const int vec_ok = (reinterpret_cast<uintptr_t>(a.grid) % (VEC * esz) == 0) &&
                      ((a.nx * (int64_t)esz) % (int64_t)(VEC * esz) == 0);
-  int nlut = (DT == 1 && vec_ok) ? lut_entries(a.H) : 0;
+  int nlut = DT == 1 ? lut_entries(a.H) : 0;
   if (nlut > 0 && lds_bytes(DT, nbins, C, a.H, nlut, NT) > 128 * 1024) nlut = 0;  // very large H
   const size_t lds = lds_bytes(DT, nbins, C, a.H, nlut, NT);
   auto k = hard3d_kernel<DT, VEC, C, TY, NT, MINW>;
