@@ -1064,7 +1064,7 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   if (ntz < 1) ntz = 1;
   if (ntz > a.nz) ntz = a.nz;
   int64_t TZ = (a.nz + ntz - 1) / ntz;
-  if (TZ < 8 && a.nz >= 8) TZ = 8;
+  if (TZ < 2 && a.nz >= 2) TZ = 2;  // a tile of one plane would re-read as many halo planes as it owns
   ntz = (a.nz + TZ - 1) / TZ;
   const int64_t ntiles = ntx * nty4 * ntz;
   const size_t esz = DT == 0 ? 1 : 4;
