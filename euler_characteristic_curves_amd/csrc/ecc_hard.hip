@@ -560,6 +560,23 @@ __device__ __forceinline__ int lut_key(float v, const LutBin& lb) {
   return __float_as_int(e.y) + ((v > e.x) ? lb.hi4 : lb.lo4);
 }
 
+// Exact key by binary search over the running max R (any thresholds): the
+// number of R_k below v, found with a fixed, wave-uniform number of steps.
+struct SearchBin {
+  const float* R;
+  int H;
+  int top;         // largest power of two <= H (0 if H == 0)
+  int base;        // LDS byte address of bin 0 for this lane's copy
+  int stride;      // bytes per bin (4 C)
+};
+
+__device__ __forceinline__ int search_key(float v, const SearchBin& sb) {
+  int k = 0;
+  for (int step = sb.top; step > 0; step >>= 1)
+    if (k + step <= sb.H && sb.R[k + step - 1] < v) k += step;
+  return sb.base + k * sb.stride;
+}
+
 template <int NT>
 __device__ __forceinline__ void build_lut(const float* R, int H, int n, float2* lut, int* ok_flag,
                                           LutBin& lb, unsigned int hist_addr, unsigned int stride) {
@@ -775,10 +792,12 @@ struct RawLut {
 // SCALAR: element loads with the column clamped to the grid, and trash keys
 // for columns past its end, for a chunk that sticks out of the grid or rows
 // that are not 16-byte aligned.
-template <int VEC, int C, int TY, bool SCALAR>
+// KEY maps a value to its key (the LDS address of this lane's counter for
+// its bin): the bucket table, or a binary search when the table is unusable.
+template <int VEC, int C, int TY, bool SCALAR, typename KEY>
 __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_t ny, int64_t nx, int64_t zs,
                                            int64_t ze, int64_t ys, int64_t xb, int lane, int lofs, int* hist,
-                                           int trash_bin, const LutBin& lb) {
+                                           int trash_bin, const LutBin& lb, KEY key) {
   static_assert(VEC == 4, "float rows are loaded as float4");
   // keys are LDS byte addresses of this lane's counters (see tele_add)
   const int trash = (int)((unsigned int)(size_t)(lds_int*)hist + 4u * (unsigned int)(C * trash_bin)) + lb.lo4;
@@ -795,24 +814,19 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
   int64_t roff[TY + 1];
 #pragma unroll
   for (int r = 0; r <= TY; ++r) roff[r] = uni64((ys + r < ny ? ys + r : ny - 1) * nx + xb - 1);
-  // SCALAR: last valid column relative to the chunk start, and this lane's
-  // four clamped byte offsets
+  // SCALAR: last valid column relative to the chunk start; the clamped
+  // offsets and column checks are recomputed where used (cheaper than
+  // keeping eight more values live through the loop)
   const int lim = (int)(nx - 1 - xb < CHUNK ? nx - 1 - xb : CHUNK - 1);
-  unsigned int coff[VEC];
-  bool cok[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    const int col = 4 * lane + j;
-    cok[j] = col <= lim;
-    coff[j] = 4u + 4u * (unsigned int)(col <= lim ? col : lim);
-  }
+  auto coff = [&](int j) { return 4u + 4u * (unsigned int)min(4 * lane + j, lim); };
+  auto cok = [&](int j) { return 4 * lane + j <= lim; };
   auto fetch = [&](RawLut& q, int64_t z, int r) {
     const char* base = reinterpret_cast<const char*>(grid + uni64((z < nz ? z : nz - 1) * plane + roff[r]));
     if constexpr (SCALAR) {
-      q.v.x = *reinterpret_cast<const float*>(base + coff[0]);
-      q.v.y = *reinterpret_cast<const float*>(base + coff[1]);
-      q.v.z = *reinterpret_cast<const float*>(base + coff[2]);
-      q.v.w = *reinterpret_cast<const float*>(base + coff[3]);
+      q.v.x = *reinterpret_cast<const float*>(base + coff(0));
+      q.v.y = *reinterpret_cast<const float*>(base + coff(1));
+      q.v.z = *reinterpret_cast<const float*>(base + coff(2));
+      q.v.w = *reinterpret_cast<const float*>(base + coff(3));
     } else {
       q.v = *reinterpret_cast<const float4*>(base + voff);
     }
@@ -820,15 +834,15 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
   };
   auto keys = [&](const RawLut& q, bool row_ok, int (&k)[VEC], int& ke) {
     if (row_ok) {
-      k[0] = lut_key(q.v.x, lb);
-      k[1] = lut_key(q.v.y, lb);
-      k[2] = lut_key(q.v.z, lb);
-      k[3] = lut_key(q.v.w, lb);
+      k[0] = key(q.v.x);
+      k[1] = key(q.v.y);
+      k[2] = key(q.v.z);
+      k[3] = key(q.v.w);
       if constexpr (SCALAR) {
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) k[j] = cok[j] ? k[j] : trash;
+        for (int j = 0; j < VEC; ++j) k[j] = cok(j) ? k[j] : trash;
       }
-      const int e = lut_key(q.e, lb);
+      const int e = key(q.e);
       ke = slot_ok ? e : trash;
     } else {
 #pragma unroll
@@ -912,6 +926,13 @@ __global__ __launch_bounds__(NT, MINW) void hard3d_kernel(HardArgs a, int nbins,
   LutBin lb;
   Lds L = setup_lds<DT, C, NT>(smem, a, nbins, nlut, bc, fb, lb);
   const bool use_lut = __builtin_amdgcn_readfirstlane(L.flag[1]) != 0;
+  SearchBin sb;
+  sb.R = L.R;
+  sb.H = a.H;
+  sb.top = 0;
+  while (sb.top * 2 <= a.H) sb.top = sb.top ? sb.top * 2 : 1;
+  sb.stride = 4 * C;
+  sb.base = (int)(size_t)(lds_int*)L.hist + lb.lo4;
 
   const T* grid = reinterpret_cast<const T*>(a.grid);
   const int64_t nz = a.nz, ny = a.ny, nx = a.nx;
@@ -931,18 +952,26 @@ __global__ __launch_bounds__(NT, MINW) void hard3d_kernel(HardArgs a, int nbins,
     const int64_t ze = zs + TZ < nz ? zs + TZ : nz;
     const int64_t xb = tx * CHUNK;
     if constexpr (DT == 1) {
+      const bool full = vok && xb + CHUNK <= nx;
       if (use_lut) {
-        if (vok && xb + CHUNK <= nx)
-          tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb);
+        auto key = [&](float v) { return lut_key(v, lb); };
+        if (full)
+          tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
         else
-          tile3d_lut<VEC, C, TY, true>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb);
-        continue;
+          tile3d_lut<VEC, C, TY, true>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
+      } else {
+        auto key = [&](float v) { return search_key(v, sb); };
+        if (full)
+          tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
+        else
+          tile3d_lut<VEC, C, TY, true>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
       }
+    } else {
+      if (vok && xb + CHUNK <= nx)
+        tile3d_fast<DT, VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, fb);
+      else
+        tile3d_generic<DT, VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lofs, L.hist, vok, bc, lane);
     }
-    if (vok && xb + CHUNK <= nx)
-      tile3d_fast<DT, VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, fb);
-    else
-      tile3d_generic<DT, VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lofs, L.hist, vok, bc, lane);
   }
   flush_and_finish<DT, C, NT>(a, nbins, L.hist, L.tmp, L.ch, L.flag, L.tot);
 }
