@@ -577,8 +577,14 @@ __device__ __forceinline__ int search_key(float v, const SearchBin& sb) {
   return sb.base + k * sb.stride;
 }
 
+// Table modes (left in the first flag word given): 0 none, 1 one threshold per bucket (entries (thr,
+// address of bin base)), 2 at most kMaxPerBucket per bucket (entries (count,
+// base index)): bin(v) = base + #{thresholds of v's bucket below v}, which is
+// exact for the same reason.
+constexpr int kMaxPerBucket = 8;
+
 template <int NT>
-__device__ __forceinline__ void build_lut(const float* R, int H, int n, float2* lut, int* ok_flag,
+__device__ __forceinline__ void build_lut(const float* R, int H, int n, float2* lut, int* flag,
                                           LutBin& lb, unsigned int hist_addr, unsigned int stride) {
   const float lo = R[0], hi = R[H - 1];
   const float INF = __builtin_inff();
@@ -594,19 +600,37 @@ __device__ __forceinline__ void build_lut(const float* R, int H, int n, float2* 
   lb.add = add;
   lb.hi = (float)(n - 1);
   lb.lut = lut;
-  if (threadIdx.x == 0) *ok_flag = ok ? 1 : 0;
+  if (threadIdx.x == 0) { flag[0] = ok ? 1 : 0; flag[1] = 1; }
   __syncthreads();
-  if (!*ok_flag) return;  // uniform: every thread read the same flag
-  bool mine = true;
+  if (!flag[0]) return;  // uniform: every thread read the same flag
+  // thresholds in the fullest bucket (counted from the first of each run, capped)
+  auto run = [&](int k, int bk) {
+    int c = 1;
+    while (c <= kMaxPerBucket && k + c < H && lut_bucket(R[k + c], lb) == bk) ++c;
+    return c;
+  };
+  int worst = 1;
+  for (int k = threadIdx.x; k < H; k += NT) {
+    const int bk = lut_bucket(R[k], lb);
+    if (k == 0 || lut_bucket(R[k - 1], lb) < bk) worst = max(worst, run(k, bk));
+  }
+  if (worst > 1) atomicMax(&flag[1], worst);
+  __syncthreads();
+  const int mode = flag[1] == 1 ? 1 : (flag[1] <= kMaxPerBucket ? 2 : 0);
+  __syncthreads();
+  if (threadIdx.x == 0) flag[0] = mode;
+  if (mode == 0) { __syncthreads(); return; }
   for (int k = threadIdx.x; k <= H; k += NT) {
     const int bprev = k > 0 ? lut_bucket(R[k - 1], lb) : -1;
     const int bk = k < H ? lut_bucket(R[k], lb) : n - 1;
-    if (k > 0 && k < H && bk <= bprev) mine = false;
-    for (int j = bprev + 1; j <= bk; ++j)
-      lut[j] = make_float2((k < H && j == bk) ? R[k] : INF, __int_as_float((int)(hist_addr + stride * (unsigned int)k)));
+    for (int j = bprev + 1; j <= bk; ++j) {
+      const bool here = k < H && j == bk;  // threshold k is the first one of bucket j
+      if (mode == 1)
+        lut[j] = make_float2(here ? R[k] : INF, __int_as_float((int)(hist_addr + stride * (unsigned int)k)));
+      else
+        lut[j] = make_float2(__int_as_float(here ? run(k, bk) : 0), __int_as_float(k));
+    }
   }
-  __syncthreads();
-  if (!mine) *ok_flag = 0;  // benign race: every writer stores 0
   __syncthreads();
 }
 
@@ -642,7 +666,7 @@ __device__ __forceinline__ Lds setup_lds(unsigned char* smem, const HardArgs& a,
   if constexpr (DT == 1) {
     if (nlut > 0)
       build_lut<NT>(L.R, a.H, nlut, L.lut, L.flag + 1, lb, (unsigned int)(size_t)(lds_int*)L.hist,
-                    4u * (unsigned int)C);
+                    4u * (unsigned int)C);  // leaves the table mode in flag[1]
     // the pair table is only needed when the bucket table is not used
     if (!L.flag[1]) build_pairs<NT>(L.R, a.H, L.P);
   }
@@ -925,7 +949,7 @@ __global__ __launch_bounds__(NT, MINW) void hard3d_kernel(HardArgs a, int nbins,
   FastBin fb;
   LutBin lb;
   Lds L = setup_lds<DT, C, NT>(smem, a, nbins, nlut, bc, fb, lb);
-  const bool use_lut = __builtin_amdgcn_readfirstlane(L.flag[1]) != 0;
+  const int lut_mode = __builtin_amdgcn_readfirstlane(L.flag[1]);
   SearchBin sb;
   sb.R = L.R;
   sb.H = a.H;
@@ -953,8 +977,21 @@ __global__ __launch_bounds__(NT, MINW) void hard3d_kernel(HardArgs a, int nbins,
     const int64_t xb = tx * CHUNK;
     if constexpr (DT == 1) {
       const bool full = vok && xb + CHUNK <= nx;
-      if (use_lut) {
+      if (lut_mode == 1) {
         auto key = [&](float v) { return lut_key(v, lb); };
+        if (full)
+          tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
+        else
+          tile3d_lut<VEC, C, TY, true>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
+      } else if (lut_mode == 2) {
+        // bucket of v, then the few thresholds sharing it
+        auto key = [&](float v) {
+          const float2 e = lb.lut[lut_bucket(v, lb)];
+          const int b0 = __float_as_int(e.y), c = __float_as_int(e.x);
+          int k = b0;
+          for (int i = 0; i < c; ++i) k += (int)(sb.R[b0 + i] < v);
+          return sb.base + k * sb.stride;
+        };
         if (full)
           tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
         else

@@ -89,6 +89,24 @@ def test_hard_threshold_counts(E, H):
     _check_hard(E, gu, (np.arange(H) * 255.0 / max(H - 1, 1)).astype(np.float32), f"u8-H{H}")
 
 
+def test_hard_threshold_spacings_3d(E):
+    """Float 3D binning for evenly spaced, quantile-spaced, heavily clustered and
+    repeated thresholds (the kernel bins by a one-per-bucket table, a small
+    per-bucket scan, or a binary search, depending on the spacing)."""
+    g = W.gaussian_random_field((33, 40, 300), 2.0, 77)
+    gmin, gmax = float(g.min()), float(g.max())
+    flat = np.sort(g.ravel()[::13].astype(np.float64))
+    cases = {
+        "linspace": W.tau_linspace(gmin, gmax, 512),
+        "quantiles": np.quantile(flat, np.linspace(0, 1, 512)).astype(np.float32),
+        "cluster": np.sort(np.concatenate([[gmin, gmax], np.linspace(0.0, 1e-3, 400)])).astype(np.float32),
+        "repeats": np.sort(np.repeat(np.linspace(gmin, gmax, 37), 7)).astype(np.float32),
+        "wide": np.sort(np.concatenate([[-1e30, 1e30], np.linspace(gmin, gmax, 100)])).astype(np.float32),
+    }
+    for name, tau in cases.items():
+        _check_hard(E, g, tau, "3d-" + name)
+
+
 def test_hard_special_values(E):
     rng = np.random.default_rng(5)
     specials = np.array([-0.0, 0.0, 1e-45, -1e-45, 1e-38, np.inf, -np.inf, 1.0, -1.0, 3e38], np.float32)
