@@ -1065,6 +1065,14 @@ int resident_blocks(const void* kernel, int nt, size_t lds) {
   return n;
 }
 
+// Workgroups worth launching for a grid of nvox voxels and nbins bins: every
+// workgroup flushes up to nbins+1 device-scope atomics, so on small grids with
+// many bins fewer, fuller workgroups finish sooner (at least one per CU).
+int64_t useful_blocks(int64_t nvox, int nbins, int cus) {
+  const int64_t v = nvox / (4 * (int64_t)(nbins + 1));
+  return v > cus ? v : cus;
+}
+
 // Threads per workgroup of the 3D float kernel.
 constexpr int kNT3 = 512;
 
@@ -1096,7 +1104,11 @@ hipError_t launch2d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   const int64_t ntx = (a.nx + CHUNK - 1) / CHUNK;
   // rows per wave: TH on large grids, fewer when that would leave the chip
   // short of workgroups (the per-wave row walk is serial)
-  const int64_t want = (int64_t)di.cus * 4;
+  int64_t want = (int64_t)di.cus * 4;
+  {
+    const int64_t u = useful_blocks(a.ny * a.nx, nbins, di.cus);
+    if (want > u) want = u;
+  }
   int64_t th = (a.ny * ntx) / (want * kWavesPerBlock);
   if (th > TH) th = TH;
   if (th < 1) th = 1;
@@ -1112,6 +1124,7 @@ hipError_t launch2d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
     if (e != hipSuccess) return e;
   }
   int64_t g = (int64_t)di.cus * resident_blocks(reinterpret_cast<const void*>(k), kBlock, lds);
+  if (g > want) g = want;
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
   hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), lds, s, a, nbins, ntx, ntiles, vec_ok, (int)th);
@@ -1125,7 +1138,11 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   const int64_t ntx = (a.nx + CHUNK - 1) / CHUNK;
   const int64_t nty4 = (a.ny + TY * WAVES - 1) / (TY * WAVES);
   // split z so that there are enough tiles to fill the chip
-  const int64_t want = (int64_t)di.cus * (4 * 256 / NT);
+  int64_t want = (int64_t)di.cus * (4 * 256 / NT);
+  {
+    const int64_t u = useful_blocks(a.nz * a.ny * a.nx, nbins, di.cus);
+    if (want > u) want = u;
+  }
   int64_t ntz = (want + ntx * nty4 - 1) / (ntx * nty4);
   if (ntz < 1) ntz = 1;
   if (ntz > a.nz) ntz = a.nz;
@@ -1145,6 +1162,7 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
     if (e != hipSuccess) return e;
   }
   int64_t g = (int64_t)di.cus * resident_blocks(reinterpret_cast<const void*>(k), NT, lds);
+  if (g > want) g = want;
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
   hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(NT), lds, s, a, nbins, ntx, nty4, TZ, ntiles,
