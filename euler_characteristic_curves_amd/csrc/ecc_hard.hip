@@ -808,8 +808,9 @@ __device__ __forceinline__ void tile3d_fast(const typename Elem<DT>::T* grid, in
 // right (only lane 63 uses it), so one load and one binning serve both edges.
 // Row and plane validity is wave-uniform and handled by branches.  The z loop
 // is unrolled twice so that planes z and z+1 swap roles instead of being copied.
+template <int VEC>
 struct RawLut {
-  float4 v;
+  float v[VEC];
   float e;
 };
 
@@ -817,12 +818,15 @@ struct RawLut {
 // for columns past its end, for a chunk that sticks out of the grid or rows
 // that are not 16-byte aligned.
 // KEY maps a value to its key (the LDS address of this lane's counter for
-// its bin): the bucket table, or a binary search when the table is unusable.
+// its bin): the bucket table, a per-bucket scan, or a binary search.
+// With VEC = 8 a wave would cover a whole row of up to 512 values, with no
+// neighbouring chunks and no edge values to load or bin.
 template <int VEC, int C, int TY, bool SCALAR, typename KEY>
 __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_t ny, int64_t nx, int64_t zs,
                                            int64_t ze, int64_t ys, int64_t xb, int lane, int lofs, int* hist,
                                            int trash_bin, const LutBin& lb, KEY key) {
-  static_assert(VEC == 4, "float rows are loaded as float4");
+  static_assert(VEC == 4 || VEC == 8, "float rows are loaded as float4");
+  constexpr bool EDGES = VEC == 4;
   // keys are LDS byte addresses of this lane's counters (see tele_add)
   const int trash = (int)((unsigned int)(size_t)(lds_int*)hist + 4u * (unsigned int)(C * trash_bin)) + lb.lo4;
   constexpr int64_t CHUNK = 64 * VEC;
@@ -830,51 +834,58 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
   const bool has_l = xb > 0, has_r = xb + CHUNK < nx;
   const bool lane0 = lane == 0;
   const bool slot_ok = lane0 ? has_l : has_r;
-  // byte offsets from the element just left of the chunk: vector at 4 + 16 lane,
-  // edge at 0 (left) or 4 (CHUNK + 1) (right); a missing edge reads the
-  // chunk's first element instead (its key is replaced by trash)
-  const unsigned int voff = 4u + 16u * (unsigned int)lane;
+  // byte offsets from the element just left of the chunk: vector at
+  // 4 + 4 VEC lane, edge at 0 (left) or 4 (CHUNK + 1) (right); a missing edge
+  // reads the chunk's first element instead (its key is replaced by trash)
+  const unsigned int voff = 4u + 4u * VEC * (unsigned int)lane;
   const unsigned int eoff = lane0 ? (has_l ? 0u : 4u) : (has_r ? 4u * (unsigned int)(CHUNK + 1) : 4u);
   int64_t roff[TY + 1];
 #pragma unroll
   for (int r = 0; r <= TY; ++r) roff[r] = uni64((ys + r < ny ? ys + r : ny - 1) * nx + xb - 1);
   // SCALAR: last valid column relative to the chunk start; the clamped
   // offsets and column checks are recomputed where used (cheaper than
-  // keeping eight more values live through the loop)
+  // keeping more values live through the loop)
   const int lim = (int)(nx - 1 - xb < CHUNK ? nx - 1 - xb : CHUNK - 1);
-  auto coff = [&](int j) { return 4u + 4u * (unsigned int)min(4 * lane + j, lim); };
-  auto cok = [&](int j) { return 4 * lane + j <= lim; };
-  auto fetch = [&](RawLut& q, int64_t z, int r) {
+  auto coff = [&](int j) { return 4u + 4u * (unsigned int)min(VEC * lane + j, lim); };
+  auto cok = [&](int j) { return VEC * lane + j <= lim; };
+  auto fetch = [&](RawLut<VEC>& q, int64_t z, int r) {
     const char* base = reinterpret_cast<const char*>(grid + uni64((z < nz ? z : nz - 1) * plane + roff[r]));
     if constexpr (SCALAR) {
-      q.v.x = *reinterpret_cast<const float*>(base + coff(0));
-      q.v.y = *reinterpret_cast<const float*>(base + coff(1));
-      q.v.z = *reinterpret_cast<const float*>(base + coff(2));
-      q.v.w = *reinterpret_cast<const float*>(base + coff(3));
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) q.v[j] = *reinterpret_cast<const float*>(base + coff(j));
     } else {
-      q.v = *reinterpret_cast<const float4*>(base + voff);
+#pragma unroll
+      for (int h = 0; h < VEC / 4; ++h) {
+        const float4 w = *reinterpret_cast<const float4*>(base + voff + 16u * h);
+        q.v[4 * h] = w.x;
+        q.v[4 * h + 1] = w.y;
+        q.v[4 * h + 2] = w.z;
+        q.v[4 * h + 3] = w.w;
+      }
     }
-    q.e = *reinterpret_cast<const float*>(base + eoff);
+    if constexpr (EDGES) q.e = *reinterpret_cast<const float*>(base + eoff);
   };
-  auto keys = [&](const RawLut& q, bool row_ok, int (&k)[VEC], int& ke) {
+  auto keys = [&](const RawLut<VEC>& q, bool row_ok, int (&k)[VEC], int& ke) {
     if (row_ok) {
-      k[0] = key(q.v.x);
-      k[1] = key(q.v.y);
-      k[2] = key(q.v.z);
-      k[3] = key(q.v.w);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) k[j] = key(q.v[j]);
       if constexpr (SCALAR) {
 #pragma unroll
         for (int j = 0; j < VEC; ++j) k[j] = cok(j) ? k[j] : trash;
       }
-      const int e = key(q.e);
-      ke = slot_ok ? e : trash;
+      if constexpr (EDGES) {
+        const int e = key(q.e);
+        ke = slot_ok ? e : trash;
+      } else {
+        ke = trash;
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < VEC; ++j) k[j] = trash;
       ke = trash;
     }
   };
-  RawLut raw[TY + 1];
+  RawLut<VEC> raw[TY + 1];
   int A[TY + 1][VEC], AE[TY + 1], B[TY + 1][VEC], BE[TY + 1];
 #pragma unroll
   for (int r = 0; r <= TY; ++r) fetch(raw[r], zs, r);
@@ -1173,6 +1184,8 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
 template <int C>
 hipError_t dispatch_f32(const HardArgs& a, int nbins, hipStream_t s, const DeviceInfo& di) {
   if (a.nz == 1) return launch2d<1, 4, C, 16>(a, nbins, s, di);
+  // (a whole-row variant, 8 values per lane without chunk edges, was measured:
+  // it needs more than 128 VGPRs even at two rows per tile)
   return launch3d<1, 4, C, 4, kNT3, 4>(a, nbins, s, di);
 }
 
