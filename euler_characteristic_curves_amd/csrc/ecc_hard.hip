@@ -808,10 +808,26 @@ __device__ __forceinline__ void tile3d_fast(const typename Elem<DT>::T* grid, in
 // right (only lane 63 uses it), so one load and one binning serve both edges.
 // Row and plane validity is wave-uniform and handled by branches.  The z loop
 // is unrolled twice so that planes z and z+1 swap roles instead of being copied.
+// Compile-time loop (DPP controls must be constants).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Value of lane R to lane 0 (row_shl:R, first row only) and of lane 63-R to
+// lane 63 (row_shr:R, last row only); other lanes keep v.
+template <int R>
+__device__ __forceinline__ int edges_to_ends(int v) {
+  const int l = __builtin_amdgcn_update_dpp(v, v, 0x100 + R, 0x1, 0xF, false);
+  return __builtin_amdgcn_update_dpp(l, v, 0x110 + R, 0x8, 0xF, false);
+}
+
 template <int VEC>
 struct RawLut {
   float v[VEC];
-  float e;
 };
 
 // SCALAR: element loads with the column clamped to the grid, and trash keys
@@ -832,13 +848,20 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
   constexpr int64_t CHUNK = 64 * VEC;
   const int64_t plane = ny * nx;
   const bool has_l = xb > 0, has_r = xb + CHUNK < nx;
-  const bool lane0 = lane == 0;
-  const bool slot_ok = lane0 ? has_l : has_r;
-  // byte offsets from the element just left of the chunk: vector at
-  // 4 + 4 VEC lane, edge at 0 (left) or 4 (CHUNK + 1) (right); a missing edge
-  // reads the chunk's first element instead (its key is replaced by trash)
+  // byte offset of the vector from the element just left of the chunk
   const unsigned int voff = 4u + 4u * VEC * (unsigned int)lane;
-  const unsigned int eoff = lane0 ? (has_l ? 0u : 4u) : (has_r ? 4u * (unsigned int)(CHUNK + 1) : 4u);
+  // Edge values (the columns just outside the chunk, needed by lanes 0 and
+  // 63) are loaded and binned once per plane for all TY+1 rows: lane r holds
+  // row r's left edge, lane 63-r row r's right edge.  Their keys carry the
+  // copy offset of the lane that uses them (0 or 63).  A missing edge (grid
+  // border) reads a valid element and gets the trash key.
+  const int erow = lane <= TY ? lane : (63 - lane <= TY ? 63 - lane : 0);
+  const bool eleft = lane <= TY;
+  const bool eok = eleft ? has_l : has_r;
+  const int64_t ecol = eleft ? (has_l ? xb - 1 : xb) : (has_r ? xb + CHUNK : xb);
+  const int64_t eoff64 = (ys + erow < ny ? ys + erow : ny - 1) * nx + ecol;  // element offset in a plane
+  const int elo = 4 * ((eleft ? 0 : 63) & (C - 1));                         // user lane's copy offset
+  const int etrash = trash - lb.lo4 + elo;
   int64_t roff[TY + 1];
 #pragma unroll
   for (int r = 0; r <= TY; ++r) roff[r] = uni64((ys + r < ny ? ys + r : ny - 1) * nx + xb - 1);
@@ -863,9 +886,11 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
         q.v[4 * h + 3] = w.w;
       }
     }
-    if constexpr (EDGES) q.e = *reinterpret_cast<const float*>(base + eoff);
   };
-  auto keys = [&](const RawLut<VEC>& q, bool row_ok, int (&k)[VEC], int& ke) {
+  auto fetch_edges = [&](float& e, int64_t z) {
+    e = grid[(z < nz ? z : nz - 1) * plane + eoff64];
+  };
+  auto keys = [&](const RawLut<VEC>& q, bool row_ok, int (&k)[VEC]) {
     if (row_ok) {
 #pragma unroll
       for (int j = 0; j < VEC; ++j) k[j] = key(q.v[j]);
@@ -873,35 +898,56 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
 #pragma unroll
         for (int j = 0; j < VEC; ++j) k[j] = cok(j) ? k[j] : trash;
       }
-      if constexpr (EDGES) {
-        const int e = key(q.e);
-        ke = slot_ok ? e : trash;
-      } else {
-        ke = trash;
-      }
     } else {
 #pragma unroll
       for (int j = 0; j < VEC; ++j) k[j] = trash;
-      ke = trash;
     }
   };
+  // edge keys of plane z for every row: one binning in the edge lanes, then
+  // row-masked DPP row shifts bring row r's left edge to lane 0 (from lane r)
+  // and its right edge to lane 63 (from lane 63-r)
+  auto edge_keys = [&](float e, bool plane_ok, int (&E)[TY + 1]) {
+    int ke = key(e) - lb.lo4 + elo;
+    ke = (plane_ok && eok && ys + erow < ny) ? ke : etrash;
+    E[0] = ke;
+    static_for<1, TY + 1>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      E[r] = edges_to_ends<r>(ke);
+    });
+  };
   RawLut<VEC> raw[TY + 1];
+  float rawe = 0.0f;
   int A[TY + 1][VEC], AE[TY + 1], B[TY + 1][VEC], BE[TY + 1];
 #pragma unroll
   for (int r = 0; r <= TY; ++r) fetch(raw[r], zs, r);
+  if constexpr (EDGES) fetch_edges(rawe, zs);
 #pragma unroll
-  for (int r = 0; r <= TY; ++r) keys(raw[r], ys + r < ny, A[r], AE[r]);
+  for (int r = 0; r <= TY; ++r) keys(raw[r], ys + r < ny, A[r]);
+  if constexpr (EDGES) {
+    edge_keys(rawe, true, AE);
+  } else {
+#pragma unroll
+    for (int r = 0; r <= TY; ++r) AE[r] = trash;
+  }
 #pragma unroll
   for (int r = 0; r <= TY; ++r) fetch(raw[r], zs + 1, r);
+  if constexpr (EDGES) fetch_edges(rawe, zs + 1);
   // one plane step: keys of plane z+1 into Y, fetch of plane z+2, rows of
   // plane z (X) against plane z+1 (Y); two steps per trip swap X and Y
   auto step = [&](int (&X)[TY + 1][VEC], int (&XE)[TY + 1], int (&Y)[TY + 1][VEC], int (&YE)[TY + 1],
                   int64_t z) {
     const bool zn = z + 1 < nz;
 #pragma unroll
-    for (int r = 0; r <= TY; ++r) keys(raw[r], zn && ys + r < ny, Y[r], YE[r]);
+    for (int r = 0; r <= TY; ++r) keys(raw[r], zn && ys + r < ny, Y[r]);
+    if constexpr (EDGES) {
+      edge_keys(rawe, zn, YE);
+    } else {
+#pragma unroll
+      for (int r = 0; r <= TY; ++r) YE[r] = trash;
+    }
 #pragma unroll
     for (int r = 0; r <= TY; ++r) fetch(raw[r], z + 2, r);
+    if constexpr (EDGES) fetch_edges(rawe, z + 2);
     rows3d<1, VEC, C, TY, true>(X, XE, XE, Y, YE, YE, ys, ny, hist, lofs);
   };
   for (int64_t z = zs; z < ze; z += 2) {
