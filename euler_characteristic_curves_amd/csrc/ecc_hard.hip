@@ -113,11 +113,6 @@ __device__ __forceinline__ int load_key1(const typename Elem<DT>::T* row, int64_
   return (row != nullptr && x >= 0 && x < nx) ? key_of<DT>(row[x], c) : c.trash;
 }
 
-// Weight of a sequence at one position: +1 at a start of a rise, -1 at its top.
-__device__ __forceinline__ int tele(int prev, int cur, int next) {
-  return (int)(next > cur) - (int)(cur > prev);
-}
-
 // ------------------------------------------------------- fast-path helpers
 // Cross-lane neighbours with DPP wave shifts (no LDS traffic).  Lane i gets
 // lane i-1's (from_left) / lane i+1's (from_right) value; the lane at the end
@@ -166,29 +161,6 @@ template <int NT>
 __device__ __forceinline__ void build_pairs(const float* R, int H, float2* P) {
   for (int k = threadIdx.x; k <= H; k += NT)
     P[k] = make_float2(k > 0 ? R[k - 1] : -__builtin_inff(), k < H ? R[k] : __builtin_inff());
-}
-
-// First k with v <= R[k] (or H) by binary search: the rare fallback of bin_fast,
-// kept out of line so the unrolled fast path stays small.
-__device__ __attribute__((noinline)) int bin_search(float v, const float* R, int H) {
-  int lo = 0, hi = H;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (v <= R[mid]) hi = mid; else lo = mid + 1;
-  }
-  return lo;
-}
-
-// One LDS read per voxel when the linear guess lands in the right bin; exact
-// fallback (binary search on R) otherwise.
-__device__ __forceinline__ int bin_fast(float v, const float2* P, const float* R, int H, float mul,
-                                        float add) {
-  float g = ceilf(fmaf(v, mul, add));
-  g = fminf(fmaxf(g, 0.0f), (float)H);  // NaN -> 0
-  int k = (int)g;
-  const float2 p = P[k];
-  if (!(p.x < v && v <= p.y)) k = bin_search(v, R, H);
-  return k;
 }
 
 // ------------------------------------------------------------ shared tail
@@ -287,19 +259,6 @@ struct FastBin {
   float mul, add;
 };
 
-template <int DT>
-__device__ __forceinline__ int fkey(typename Elem<DT>::T v, const FastBin& fb) {
-  if constexpr (DT == 0) {
-    (void)fb;
-    return (int)v;
-  } else {
-    return bin_fast(v, fb.P, fb.R, fb.H, fb.mul, fb.add);
-  }
-}
-
-// Keys of a fetched row.  The loaded registers are always consumed (validity
-// is applied afterwards with selects), so no load is left pending on any
-// path.  CHECK=false skips the selects for rows known to be inside the grid.
 // Fast bin guess for one float (first k with v <= R[k] when the thresholds
 // are close to uniform): 4 VALU ops, clamped to [0, H] (NaN -> 0).
 __device__ __forceinline__ int bin_guess(float v, const FastBin& fb) {

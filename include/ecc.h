@@ -89,7 +89,13 @@ extern "C" {
 int ecc_hard_2d(const void* grid, int dtype, int64_t ny, int64_t nx, const float* tau, int32_t H,
                 int64_t* out, void* ws, size_t ws_bytes, void* stream);
 
-/* Hard ECC of a 3D grid [nz][ny][nx]; otherwise as ecc_hard_2d. */
+/*
+ * Hard ECC of a 3D grid [nz][ny][nx]; otherwise as ecc_hard_2d.
+ * Speed (not results) depends on the thresholds for float32 grids: finite,
+ * roughly evenly spaced thresholds (e.g. linspace(min, max, H)) bin through an
+ * exact one-read table; thresholds that crowd together (e.g. data quantiles)
+ * take a short per-bucket scan or a binary search, about 2x-6x slower.
+ */
 int ecc_hard_3d(const void* grid, int dtype, int64_t nz, int64_t ny, int64_t nx, const float* tau,
                 int32_t H, int64_t* out, void* ws, size_t ws_bytes, void* stream);
 
