@@ -24,6 +24,11 @@ Pinning status (what checks this oracle against something other than itself):
                                grid closed form, lambda -> infinity limit.
   * ecc_soft_bwd_tau       -- pinned: central finite differences of the
                                forward, integral identity (sum of signs = 1).
+  * ecc_soft_bwd_grid(_at) -- pinned: central finite differences of a
+                               per-cell brute-force forward with respect to
+                               each voxel on tie-free grids, the sum rule
+                               (translating the grid by s moves every cell
+                               value by s), per-voxel vs scatter agreement.
   * at the 256^3 soft size the only check is the per-cell vs grouped
     agreement of this same oracle: parity unpinned beyond that.
 """
@@ -42,5 +47,7 @@ from .ecc import (  # noqa: F401
     ecc_soft_bwd_tau,
     ecc_soft_bwd_at,
     ecc_soft_bwd_at_many,
+    ecc_soft_bwd_grid,
+    ecc_soft_bwd_grid_at,
     sigmoid,
 )

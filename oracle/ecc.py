@@ -27,7 +27,7 @@ __all__ = [
     "cell_values", "cell_counts", "first_k_bins", "ecc_hard", "ecc_at",
     "sigmoid", "ecc_soft", "ecc_soft_percell", "ecc_soft_at",
     "ecc_soft_bwd_tau", "ecc_soft_bwd_at", "ecc_at_many", "ecc_soft_at_many",
-    "ecc_soft_bwd_at_many",
+    "ecc_soft_bwd_at_many", "ecc_soft_bwd_grid", "ecc_soft_bwd_grid_at",
 ]
 
 
@@ -315,3 +315,90 @@ def ecc_soft_bwd_at(grid, t, lam, g, slab=32):
         for val, dim in _slab_cells(sub, keep):
             acc += (-1) ** dim * float(_dsig(lam * (t - val.astype(np.float64))).sum())
     return g * lam * acc
+
+
+# ------------------------------------------------------------ grid gradient
+# The differentiable ECC layer of the page ("Method / Key designs") has an
+# analytic backward; the gradient with respect to the grid values follows from
+# the same definition.  A cell's value is the max of its corners, so d v_c /
+# d X(p) is 1 for the corner holding the max and 0 for the others.  Ties (a
+# reading; the page does not discuss them): the max goes to the first corner
+# in index order (C order, x fastest) among those holding it, so the gradient
+# is one subgradient of the max, the one a first-index argmax picks.
+
+def _h_of(u, t, lam, g, chunk=1 << 15):
+    """h(u) = sum_k g_k sigma(x) sigma(-x), x = lam (tau_k - u), for each u (float64)."""
+    out = np.empty(u.size, dtype=np.float64)
+    for i in range(0, u.size, chunk):
+        x = lam * (t[None, :] - u[i:i + chunk, None])
+        out[i:i + chunk] = _dsig(x) @ g
+    return out
+
+
+def _grad_inputs(grid, tau, lam, grad_out):
+    grid = _check_grid(grid)
+    t = _tau64(tau)
+    lam = _check_lambda(lam)
+    g = np.asarray(grad_out).astype(np.float32).astype(np.float64)
+    if g.shape != t.shape:
+        raise ValueError("grad_out must have the shape of tau")
+    return grid, t, lam, g
+
+
+def ecc_soft_bwd_grid(grid, tau, lam, grad_out):
+    """dL/dX(p) for L = sum_k g_k S_k, S = ecc_soft(grid, tau, lam).
+
+    d S_k / d v_c = -lam sigma(x) sigma(-x) with x = lam (tau_k - v_c), and
+    d v_c / d X(p) = [p is the argmax corner of c]; so every cell passes
+    -lam (-1)^dim(c) h(v_c) to its argmax corner, h(v) = sum_k g_k sigma sigma'.
+    Written as that scatter, cell type by cell type (float64).
+    """
+    grid, t, lam, g = _grad_inputs(grid, tau, lam, grad_out)
+    X = grid.astype(np.float64)
+    shape = X.shape
+    index = np.arange(X.size, dtype=np.int64).reshape(shape)
+    out = np.zeros(X.size, dtype=np.float64)
+    for ext in itertools.product((0, 1), repeat=X.ndim):
+        anchors = [n - e for n, e in zip(shape, ext)]
+        if min(anchors) <= 0:
+            continue
+        offs = list(itertools.product(*[range(e + 1) for e in ext]))  # increasing index order
+        vals = np.stack([X[tuple(slice(o, o + a) for o, a in zip(off, anchors))] for off in offs])
+        idxs = np.stack([index[tuple(slice(o, o + a) for o, a in zip(off, anchors))] for off in offs])
+        am = np.argmax(vals, axis=0)  # first corner holding the max
+        v = np.take_along_axis(vals, am[None], 0)[0].ravel()
+        tgt = np.take_along_axis(idxs, am[None], 0)[0].ravel()
+        u, inv = np.unique(v, return_inverse=True)
+        contrib = -lam * (-1) ** sum(ext) * _h_of(u, t, lam, g)[inv]
+        np.add.at(out, tgt, contrib)
+    return out.reshape(shape)
+
+
+def ecc_soft_bwd_grid_at(grid, points, tau, lam, grad_out):
+    """ecc_soft_bwd_grid at selected voxels (a list of index tuples), float64.
+
+    Per voxel p: every cell holding p whose max goes to p has value X(p), so
+    dL/dX(p) = -lam c(p) h(X(p)) with c(p) the signed count of those cells.
+    The cells are enumerated one by one around p (for large grids, where the
+    full scatter does not fit).
+    """
+    grid, t, lam, g = _grad_inputs(grid, tau, lam, grad_out)
+    X = grid.astype(np.float64)
+    shape = X.shape
+    res = []
+    for p in points:
+        p = tuple(int(c) for c in p)
+        c = 0
+        for ext in itertools.product((0, 1), repeat=X.ndim):
+            for o in itertools.product(*[range(e + 1) for e in ext]):
+                a = tuple(pi - oi for pi, oi in zip(p, o))
+                if any(ai < 0 or ai + e >= n for ai, e, n in zip(a, ext, shape)):
+                    continue  # cell sticks out of the grid
+                corners = [tuple(ai + qi for ai, qi in zip(a, q))
+                           for q in itertools.product(*[range(e + 1) for e in ext])]
+                best = max(corners, key=lambda q: (X[q], -np.ravel_multi_index(q, shape)))
+                if best == p:
+                    c += (-1) ** sum(ext)
+        h = float(_h_of(np.array([X[p]]), t, lam, g)[0]) if c else 0.0
+        res.append(-lam * c * h)
+    return np.array(res, dtype=np.float64)

@@ -305,6 +305,92 @@ def test_soft_backward_integrates_to_euler_sum():
     assert abs(integral - 1.0) < 1e-4
 
 
+def _distinct_grid(shape, seed):
+    """Float32-exact values k/n in random order: no ties, gaps far above the FD step."""
+    n = int(np.prod(shape))
+    rng = np.random.default_rng(seed)
+    return (rng.permutation(n).astype(np.float64) / n).reshape(shape)
+
+
+@pytest.mark.parametrize("shape", [(4, 5), (3, 4, 5)])
+def test_soft_grid_gradient_finite_differences(shape):
+    """dL/dX(p) of L = sum_k g_k S_k against central differences of the per-cell
+    forward written out by hand, voxel by voxel, on tie-free grids."""
+    g = _distinct_grid(shape, 93)
+    rng = np.random.default_rng(94)
+    lam = 11.0
+    tau = np.linspace(-0.1, 1.1, 9).astype(np.float32)
+    gout = rng.standard_normal(tau.size).astype(np.float32)
+    got = oracle.ecc_soft_bwd_grid(g, tau, lam, gout)
+    h = 1e-6
+    gw = gout.astype(np.float64)
+    for p in np.ndindex(*shape):
+        up = g.copy()
+        up[p] += h
+        dn = g.copy()
+        dn[p] -= h
+        fd = float(np.dot(gw, np.subtract(pins.soft_by_hand(up, tau, lam), pins.soft_by_hand(dn, tau, lam)))) / (2 * h)
+        assert abs(fd - got[p]) < 1e-6 * max(1.0, abs(got[p])), (p, fd, got[p])
+    pts = [p for p in np.ndindex(*shape)][::3]
+    np.testing.assert_allclose(oracle.ecc_soft_bwd_grid_at(g, pts, tau, lam, gout),
+                               [got[p] for p in pts], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("shape", [(5, 7), (3, 4, 6)])
+def test_soft_grid_gradient_constant_grid(shape):
+    """On a constant grid every cell's corners tie and the first corner in index
+    order is the cell's anchor; the anchors' signed counts cancel everywhere but
+    at the last voxel, which takes the whole box's Euler characteristic (1):
+    dL/dX = -lam h(v) there and 0 elsewhere."""
+    v = 0.375
+    g = np.full(shape, v, np.float32)
+    lam = 6.0
+    tau = np.array([0.0, 0.3, 0.375, 0.5, 1.0], np.float32)
+    gout = np.array([1.0, -2.0, 0.5, 3.0, 0.25], np.float32)
+    got = oracle.ecc_soft_bwd_grid(g, tau, lam, gout)
+    want = np.zeros(shape)
+    want[tuple(n - 1 for n in shape)] = -lam * sum(
+        float(gk) * pins._sig(lam * (float(t) - v)) * (1 - pins._sig(lam * (float(t) - v)))
+        for t, gk in zip(tau, gout))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
+    corners = [tuple(0 for _ in shape), tuple(n - 1 for n in shape), tuple(n // 2 for n in shape)]
+    np.testing.assert_allclose(oracle.ecc_soft_bwd_grid_at(g, corners, tau, lam, gout),
+                               [want[c] for c in corners], rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("kind", ["random", "plateaus"])
+def test_soft_grid_gradient_sum_rule(kind):
+    """Moving every voxel and every threshold by the same s leaves each S_k
+    unchanged, so sum_p dL/dX(p) = -sum_k dL/dtau_k; holds with ties too,
+    since every cell hands its derivative to exactly one corner."""
+    rng = np.random.default_rng(95)
+    if kind == "random":
+        g = rng.random((6, 5, 7)).astype(np.float32)
+    else:
+        g = (rng.integers(0, 4, (6, 5, 7)) / 4).astype(np.float32)
+    lam = 8.0
+    tau = np.linspace(-0.2, 1.2, 15).astype(np.float32)
+    gout = rng.standard_normal(tau.size).astype(np.float32)
+    gx = oracle.ecc_soft_bwd_grid(g, tau, lam, gout)
+    gt = oracle.ecc_soft_bwd_tau(g, tau, lam, gout)
+    assert abs(gx.sum() + gt.sum()) < 1e-10 * max(1.0, np.abs(gt).sum())
+
+
+def test_soft_grid_gradient_is_local():
+    """Changing one voxel changes the gradient only where a cell holding that
+    voxel can send its derivative: the voxel's 3x3x3 neighbourhood."""
+    rng = np.random.default_rng(96)
+    g = rng.random((7, 8, 9)).astype(np.float32)
+    tau = np.linspace(0, 1, 6).astype(np.float32)
+    gout = rng.standard_normal(6).astype(np.float32)
+    a = oracle.ecc_soft_bwd_grid(g, tau, 5.0, gout)
+    g2 = g.copy()
+    g2[3, 4, 5] = 2.0
+    b = oracle.ecc_soft_bwd_grid(g2, tau, 5.0, gout)
+    diff = np.argwhere(np.abs(a - b) > 0)
+    assert diff.size and np.all(np.abs(diff - [3, 4, 5]) <= 1)
+
+
 def test_oracle_rejects_bad_input():
     with pytest.raises(ValueError):
         oracle.ecc_hard(np.zeros((2, 2, 2, 2)), [0.0])
