@@ -11,7 +11,7 @@ __version__ = "0.1.0"
 
 _API = (
     "ecc_hard_2d", "ecc_hard_3d", "ecc_hard", "ecc_soft_fwd", "ecc_soft_bwd_tau",
-    "workspace_bytes", "get_workspace", "EccError", "SoftECC", "soft_ecc",
+    "ecc_soft_bwd_grid", "workspace_bytes", "get_workspace", "EccError", "SoftECC", "soft_ecc",
 )
 
 __all__ = list(_API)

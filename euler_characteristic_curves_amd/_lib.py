@@ -26,7 +26,7 @@ ECC_OP_SOFT_BWD = 2
 ECC_MAX_THRESHOLDS = 8192
 
 EXPORTS = (
-    "ecc_hard_2d", "ecc_hard_3d", "ecc_soft_fwd", "ecc_soft_bwd_tau",
+    "ecc_hard_2d", "ecc_hard_3d", "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
     "ecc_workspace_bytes", "ecc_status_string", "ecc_last_error", "ecc_version",
 )
 
@@ -55,6 +55,8 @@ def _load():
     lib.ecc_soft_fwd.restype = I
     lib.ecc_soft_bwd_tau.argtypes = [P, I32, P, P, I32, F, P, P, P, SZ, P]
     lib.ecc_soft_bwd_tau.restype = I
+    lib.ecc_soft_bwd_grid.argtypes = [P, I32, P, P, I32, F, P, P, P]
+    lib.ecc_soft_bwd_grid.restype = I
     lib.ecc_workspace_bytes.argtypes = [I, I32, P, I32]
     lib.ecc_workspace_bytes.restype = SZ
     lib.ecc_status_string.argtypes = [I]

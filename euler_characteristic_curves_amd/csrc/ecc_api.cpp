@@ -48,8 +48,11 @@ int check_hard(const void* grid, int dtype, int64_t nz, int64_t ny, int64_t nx, 
   return ECC_OK;
 }
 
+// Checks shared by the soft entry points; the workspace is checked only when
+// `with_ws` (the grid gradient needs none).
 int check_soft(const float* grid, int32_t ndim, const int64_t* shape, const float* tau, int32_t H,
-               float lambda, const void* out, const void* ws, size_t ws_bytes, int64_t dims[3]) {
+               float lambda, const void* out, const void* ws, size_t ws_bytes, int64_t dims[3],
+               bool with_ws = true) {
   g_err[0] = 0;
   if (!grid) return fail(ECC_E_NULL, "%sgrid is NULL");
   if (!shape) return fail(ECC_E_NULL, "%sshape is NULL");
@@ -68,6 +71,7 @@ int check_soft(const float* grid, int32_t ndim, const int64_t* shape, const floa
     return fail(ECC_E_NTHRESH, "%sH=%lld outside [1, %lld]", nullptr, H, ECC_MAX_THRESHOLDS);
   if (!(lambda > 0.0f) || !isfinite(lambda))
     return fail(ECC_E_LAMBDA, "%slambda must be finite and > 0");
+  if (!with_ws) return ECC_OK;
   if (!ws) return fail(ECC_E_WORKSPACE, "%sworkspace is NULL");
   const size_t need = ecc::workspace_bytes(H);
   if (ws_bytes < need)
@@ -138,6 +142,16 @@ int ecc_soft_bwd_tau(const float* grid, int32_t ndim, const int64_t* shape, cons
   if (!grad_out) return fail(ECC_E_NULL, "%sgrad_out is NULL");
   ecc::SoftArgs a{grid, d[0], d[1], d[2], tau, H, lambda, grad_out, grad_tau, ws};
   return hip_status(ecc::launch_soft(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int ecc_soft_bwd_grid(const float* grid, int32_t ndim, const int64_t* shape, const float* tau,
+                      int32_t H, float lambda, const float* grad_out, float* grad_grid, void* stream) {
+  int64_t d[3];
+  int st = check_soft(grid, ndim, shape, tau, H, lambda, grad_grid, nullptr, 0, d, false);
+  if (st != ECC_OK) return st;
+  if (!grad_out) return fail(ECC_E_NULL, "%sgrad_out is NULL");
+  ecc::GradArgs a{grid, d[0], d[1], d[2], tau, H, lambda, grad_out, grad_grid};
+  return hip_status(ecc::launch_soft_grad(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t ecc_workspace_bytes(int op, int32_t ndim, const int64_t* shape, int32_t H) {

@@ -8,6 +8,16 @@
 
 namespace ecc {
 
+// ---------------------------------------------------------------- exp2
+// 2^a for |a| well inside the float range, accurate to ~1 ulp: split off the
+// integer part in float64 so the float exp2 only sees [0, 1).
+__device__ __forceinline__ float exp2_split(double a) {
+  a = fmin(fmax(a, -300.0), 300.0);
+  const double n = floor(a);
+  const float f = (float)(a - n);
+  return ldexpf(exp2f(f), (int)n);
+}
+
 // ---------------------------------------------------------------- atomics
 __device__ __forceinline__ long long agent_load(const long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -45,6 +45,16 @@ struct SoftArgs {
   void* ws;
 };
 
+struct GradArgs {
+  const float* grid;
+  int64_t nz, ny, nx;  // nz = 1 for 2D
+  const float* tau;
+  int H;
+  float lambda;
+  const float* grad_out;
+  float* out;  // grad_grid, one value per voxel
+};
+
 struct DeviceInfo {
   int cus;
   size_t lds_bytes;
@@ -55,5 +65,6 @@ hipError_t device_info(DeviceInfo* info);
 
 hipError_t launch_hard(const HardArgs& a, hipStream_t stream);
 hipError_t launch_soft(const SoftArgs& a, hipStream_t stream);
+hipError_t launch_soft_grad(const GradArgs& a, hipStream_t stream);
 
 }  // namespace ecc

@@ -37,15 +37,6 @@ constexpr int kTileVox = 1024;          // voxels per tile
 constexpr int kTermCap = 4 * kTileVox;  // at most 4 terms per voxel
 constexpr int kChunk = 256;             // thresholds per sweep chunk (4 per lane)
 
-// 2^a for |a| well inside the float range, accurate to ~1 ulp: split off the
-// integer part in float64 so the float exp2 only sees [0, 1).
-__device__ __forceinline__ float exp2_split(double a) {
-  a = fmin(fmax(a, -300.0), 300.0);
-  const double n = floor(a);
-  const float f = (float)(a - n);
-  return ldexpf(exp2f(f), (int)n);
-}
-
 struct Term {
   float a;  // F = 2^{L (v - c)} (factored) or the value v (direct)
   float w;  // summed sign

@@ -14,7 +14,7 @@ from ._lib import EccError, check, lib
 
 __all__ = [
     "ecc_hard_2d", "ecc_hard_3d", "ecc_hard", "ecc_soft_fwd", "ecc_soft_bwd_tau",
-    "workspace_bytes", "get_workspace", "EccError", "SoftECC", "soft_ecc",
+    "ecc_soft_bwd_grid", "workspace_bytes", "get_workspace", "EccError", "SoftECC", "soft_ecc",
 ]
 
 _WS = {}
@@ -165,8 +165,29 @@ def ecc_soft_bwd_tau(grid, tau, lam, grad_out, grad_tau=None, ws=None):
     return grad_tau
 
 
+def ecc_soft_bwd_grid(grid, tau, lam, grad_out, grad_grid=None):
+    """dL/dgrid of the soft ECC, float32 of the grid's shape (see include/ecc.h)."""
+    _dev_tensor(grid, "grid", torch.float32)
+    _dev_tensor(tau, "tau", torch.float32, grid.device)
+    _dev_tensor(grad_out, "grad_out", torch.float32, grid.device)
+    H = tau.numel()
+    if grad_out.numel() != H:
+        raise ValueError("grad_out must have H elements")
+    if grad_grid is None:
+        grad_grid = torch.empty_like(grid)
+    _dev_tensor(grad_grid, "grad_grid", torch.float32, grid.device)
+    if grad_grid.shape != grid.shape:
+        raise ValueError("grad_grid must have the grid's shape")
+    shp = _shape_arr(grid)
+    s = _stream(grid)
+    check(lib.ecc_soft_bwd_grid(_ptr(grid), grid.dim(), ctypes.cast(shp, ctypes.c_void_p), _ptr(tau), H,
+                                float(lam), _ptr(grad_out), _ptr(grad_grid), ctypes.c_void_p(s.cuda_stream)),
+          "ecc_soft_bwd_grid")
+    return grad_grid
+
+
 class SoftECC(torch.autograd.Function):
-    """Autograd wrapper: soft ECC with learnable thresholds (grid gradient not provided)."""
+    """Autograd wrapper: soft ECC, differentiable in the thresholds and the grid."""
 
     @staticmethod
     def forward(ctx, grid, tau, lam):
@@ -177,13 +198,14 @@ class SoftECC(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_out):
         grid, tau = ctx.saved_tensors
-        if ctx.needs_input_grad[0]:
-            raise NotImplementedError("the gradient with respect to the grid is not implemented")
-        g = ecc_soft_bwd_tau(grid.detach().contiguous(), tau.detach().contiguous(), ctx.lam,
-                             grad_out.contiguous())
-        return None, g, None
+        grid = grid.detach().contiguous()
+        tau = tau.detach().contiguous()
+        grad_out = grad_out.contiguous()
+        g_grid = ecc_soft_bwd_grid(grid, tau, ctx.lam, grad_out) if ctx.needs_input_grad[0] else None
+        g_tau = ecc_soft_bwd_tau(grid, tau, ctx.lam, grad_out) if ctx.needs_input_grad[1] else None
+        return g_grid, g_tau, None
 
 
 def soft_ecc(grid, tau, lam):
-    """Soft ECC as an autograd op (differentiable in tau)."""
+    """Soft ECC as an autograd op (differentiable in the grid and in tau)."""
     return SoftECC.apply(grid, tau, lam)

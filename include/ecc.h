@@ -127,6 +127,27 @@ int ecc_soft_bwd_tau(const float* grid, int32_t ndim, const int64_t* shape, cons
                      size_t ws_bytes, void* stream);
 
 /*
+ * Soft ECC backward with respect to the grid values.
+ *   grad_out   device float32[H]: dL/dout
+ *   grad_grid  device float32, the grid's shape: OVERWRITTEN with dL/dgrid.
+ * A cell's value is the max of its corners, so its derivative goes to the
+ * corner holding the max; among equal maxima, to the first in index order
+ * (x fastest), i.e. one subgradient of the max.  Hence
+ *   grad_grid[p] = -lambda * c(p) * sum_k grad_out[k] s(x)(1 - s(x)),
+ *   x = lambda * (tau_k - grid[p]),  s = sigmoid,
+ * with c(p) the sum of (-1)^dim(c) over the cells whose derivative goes to p
+ * (cells met inside p's 3x3(x3) block; voxels with c(p) = 0 get 0).
+ * Sums are float32 per voxel; every voxel is written exactly once, so the
+ * result does not depend on scheduling.  Needs no workspace: it may run
+ * concurrently with any other call that does not write its inputs.  The
+ * values of grad_out are taken as finite.  One kernel launch.
+ * (Section "Method / Key designs / differentiable ECC layer" gives the
+ * relaxation; the gradient with respect to the grid follows from it.)
+ */
+int ecc_soft_bwd_grid(const float* grid, int32_t ndim, const int64_t* shape, const float* tau,
+                      int32_t H, float lambda, const float* grad_out, float* grad_grid, void* stream);
+
+/*
  * Bytes of workspace needed by an operation (ECC_OP_*) for a grid of `ndim`
  * dimensions `shape` (host array; may be NULL, the size does not depend on
  * it today) and H thresholds.  Returns 0 for invalid op/H.

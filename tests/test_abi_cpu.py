@@ -26,8 +26,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
-        "ecc_hard_2d", "ecc_hard_3d", "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_workspace_bytes",
-        "ecc_status_string", "ecc_last_error", "ecc_version"])
+        "ecc_hard_2d", "ecc_hard_3d", "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
+        "ecc_workspace_bytes", "ecc_status_string", "ecc_last_error", "ecc_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -116,6 +116,28 @@ def test_soft_argument_errors(L, bwd):
     assert soft(L, ws=None, bwd=bwd) == L.ECC_E_WORKSPACE
     if bwd:
         assert soft(L, gout=None, bwd=True) == L.ECC_E_NULL
+
+
+def soft_grid(L, ndim=3, shape=(4, 4, 4), lam=1.0, H=4, grid=FAKE, tau=FAKE, gout=FAKE, out=FAKE):
+    arr = (ctypes.c_int64 * max(1, len(shape)))(*shape) if shape is not None else None
+    sp = ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None
+    return L.lib.ecc_soft_bwd_grid(grid, ndim, sp, tau, H, lam, gout, out, None)
+
+
+def test_soft_grid_argument_errors(L):
+    assert soft_grid(L, grid=None) == L.ECC_E_NULL
+    assert soft_grid(L, shape=None) == L.ECC_E_NULL
+    assert soft_grid(L, tau=None) == L.ECC_E_NULL
+    assert soft_grid(L, out=None) == L.ECC_E_NULL
+    assert soft_grid(L, gout=None) == L.ECC_E_NULL
+    assert b"grad_out" in L.lib.ecc_last_error()
+    assert soft_grid(L, ndim=4, shape=(2, 2, 2, 2)) == L.ECC_E_SHAPE
+    assert soft_grid(L, ndim=2, shape=(0, 3)) == L.ECC_E_SHAPE
+    assert soft_grid(L, shape=(1 << 14, 1 << 14, 1 << 14)) == L.ECC_E_SHAPE
+    for lam in (0.0, -2.0, math.inf, math.nan):
+        assert soft_grid(L, lam=lam) == L.ECC_E_LAMBDA
+    assert soft_grid(L, H=0) == L.ECC_E_NTHRESH
+    assert soft_grid(L, H=8193) == L.ECC_E_NTHRESH
 
 
 def test_binding_rejects_cpu_tensors():
