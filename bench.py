@@ -10,8 +10,9 @@ steps cannot be served from the 256 MB Infinity Cache.
 Also reported on the same JSON line: per-kernel durations (mean of
 back-to-back launches, and min / median of individually timed launches, HIP
 events on the launch stream) and the roofline of each hard kernel; the other
-grid sizes (128^2, 1024^2, 1024^3) as context; the soft forward / backward at
-256^3 (H=256, lambda=50) with their VALU-issue fraction; and the CPU oracle
+grid sizes (128^2, 1024^2, 1024^3) as context; the soft forward and its
+backward with respect to the thresholds and to the grid at 256^3 (H=256,
+lambda=50) with their VALU-issue fraction; and the CPU oracle
 timed on a bounded sample of the same workloads (cpu_baseline), on one core
 and on all cores, before the GPU is touched.
 
@@ -51,6 +52,8 @@ KERNEL_SOURCES = ("euler_characteristic_curves_amd/csrc/ecc_hard.hip",
                   "euler_characteristic_curves_amd/csrc/ecc_internal.hpp")
 TRAFFIC_PROFILE = "profiles/hard3d_512cube_f32_traffic.md"
 SOFT_SOURCES = ("euler_characteristic_curves_amd/csrc/ecc_soft.hip",
+                "euler_characteristic_curves_amd/csrc/ecc_soft_grad.hip",
+                "euler_characteristic_curves_amd/csrc/ecc_star.hpp",
                 "euler_characteristic_curves_amd/csrc/ecc_device.hpp",
                 "euler_characteristic_curves_amd/csrc/ecc_internal.hpp")
 SQ_PROFILE = "profiles/ecc_kernels_bench_sq_counters.md"
@@ -103,19 +106,23 @@ def recorded_traffic():
 
 
 def recorded_soft_valu():
-    """(forward, backward) VALU wave-instructions per soft launch at 256^3, H=256.
+    """(forward, tau-backward, grid-backward) VALU wave-instructions per soft
+    launch at 256^3, H=256.
 
-    The count is fixed by the kernel and its input; it comes from the committed
-    rocprofv3 SQ_INSTS_VALU profile and is used only while the soft sources
-    hash to the value recorded there.
+    The counts are fixed by the kernels and their input; they come from the
+    committed rocprofv3 SQ_INSTS_VALU profile and are used only while the soft
+    sources hash to the value recorded there.
     """
     fields = profile_fields(SQ_PROFILE)
     if fields.get("soft_source_sha256") != source_hash(SOFT_SOURCES):
-        return None, None
-    try:
-        return float(fields["soft_fwd_valu_wave_instr"]), float(fields["soft_bwd_valu_wave_instr"])
-    except (KeyError, ValueError):
-        return None, None
+        return None, None, None
+    out = []
+    for key in ("soft_fwd_valu_wave_instr", "soft_bwd_valu_wave_instr", "soft_grad_valu_wave_instr"):
+        try:
+            out.append(float(fields[key]))
+        except (KeyError, ValueError):
+            out.append(None)
+    return tuple(out)
 
 
 def traffic_run():
@@ -355,21 +362,33 @@ def main():
         dgs, dts = torch.from_numpy(gs).to(dev), torch.from_numpy(ts).to(dev)
         dgo = torch.from_numpy(extra["grad_out"]).to(dev)
         lam = extra["lam"]
+        dgg = torch.empty_like(dgs)
         E.ecc_soft_fwd(dgs, dts, lam)
         E.ecc_soft_bwd_tau(dgs, dts, lam, dgo)
+        E.ecc_soft_bwd_grid(dgs, dts, lam, dgo, dgg)
         msf = timed(torch, lambda i: E.ecc_soft_fwd(dgs, dts, lam), args.soft_reps)
         msb = timed(torch, lambda i: E.ecc_soft_bwd_tau(dgs, dts, lam, dgo), args.soft_reps)
+        msg = timed(torch, lambda i: E.ecc_soft_bwd_grid(dgs, dts, lam, dgo, dgg), args.soft_reps)
+        torch.cuda.synchronize()
+        grad_nonzero = int(torch.count_nonzero(dgg).item())
         pairs = n_cells(gs.shape) * ts.size
-        vf, vb = recorded_soft_valu()
+        vf, vb, vg = recorded_soft_valu()
+
+        def frac(v, ms):
+            return None if v is None else v / (ms * 1e-3) / VALU_WAVE_INSTR_PEAK
+
         soft = {
             "workload": "soft ECC 256^3 float32 uniform, H=256, lambda=50",
             "fwd_ms": msf, "bwd_ms": msb, "fwd_plus_bwd_ms": msf + msb,
             "cell_threshold_pairs": pairs,
             "fwd_pairs_per_s": pairs / (msf * 1e-3), "bwd_pairs_per_s": pairs / (msb * 1e-3),
+            "bwd_grid_ms": msg,
+            "bwd_grid_voxels_per_s": gs.size / (msg * 1e-3),
+            "bwd_grid_nonzero_voxels": grad_nonzero,
+            "bwd_grid_voxel_threshold_pairs_per_s": grad_nonzero * ts.size / (msg * 1e-3),
             "roofline": {"bound": "valu", "unit": "wave64 VALU instr/s", "peak": VALU_WAVE_INSTR_PEAK,
-                         "fwd_frac": None if vf is None else vf / (msf * 1e-3) / VALU_WAVE_INSTR_PEAK,
-                         "bwd_frac": None if vb is None else vb / (msb * 1e-3) / VALU_WAVE_INSTR_PEAK,
-                         "valu_instr_per_launch": {"fwd": vf, "bwd": vb}},
+                         "fwd_frac": frac(vf, msf), "bwd_frac": frac(vb, msb), "bwd_grid_frac": frac(vg, msg),
+                         "valu_instr_per_launch": {"fwd": vf, "bwd": vb, "bwd_grid": vg}},
         }
 
     vox_step = n3 + n4

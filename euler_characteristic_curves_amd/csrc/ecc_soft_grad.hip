@@ -139,7 +139,8 @@ __global__ __launch_bounds__(kGradNT) void soft_grad_kernel(GradArgs p, int64_t 
   float2* T = reinterpret_cast<float2*>(queues + kGradWaves * kQueueCap);
   float* red = reinterpret_cast<float*>(smem);                          // setup only, 3 x kGradNT
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = p.H, Hp = (H + 1) & ~1;
   const float INF = __builtin_inff();
 
@@ -199,10 +200,22 @@ __global__ __launch_bounds__(kGradNT) void soft_grad_kernel(GradArgs p, int64_t 
   QEntry* q = queues + wave * kQueueCap;
   int count = 0;  // wave-uniform
   const int64_t wstride = (int64_t)gridDim.x * kGradWaves;
-  for (int64_t seg = (int64_t)blockIdx.x * kGradWaves + wave; seg < nseg; seg += wstride) {
+  // (z0, y0, x0) of the segment's first voxel, advanced by the grid stride
+  // S = wstride * 64 voxels with a mixed-radix add (no division in the loop)
+  int64_t seg = (int64_t)blockIdx.x * kGradWaves + wave;
+  int64_t x0 = 0, y0 = 0, z0 = 0, sx = 0, sy = 0, sz = 0;
+  if (seg < nseg) {
+    const int64_t i0 = seg * 64, r0 = i0 / nx;
+    x0 = i0 - r0 * nx;
+    z0 = r0 / ny;
+    y0 = r0 - z0 * ny;
+    const int64_t S = wstride * 64, rs = S / nx;
+    sx = S - rs * nx;
+    sz = rs / ny;
+    sy = rs - sz * ny;
+  }
+  for (; seg < nseg; seg += wstride) {
     const int64_t i0 = seg * 64;
-    const int64_t r0 = i0 / nx, x0 = i0 - r0 * nx;
-    const int64_t z0 = r0 / ny, y0 = r0 - z0 * ny;
     int64_t x, y;
     const int64_t qy = div_near(x0 + lane, nx, &x);
     const int64_t qz = div_near(y0 + qy, ny, &y);
@@ -270,6 +283,17 @@ __global__ __launch_bounds__(kGradNT) void soft_grad_kernel(GradArgs p, int64_t 
       sweep(g, q + (count - kBatch), kBatch, lane);
       count -= kBatch;
       wave_lds_sync();
+    }
+    x0 += sx;
+    y0 += sy;
+    if (x0 >= nx) {
+      x0 -= nx;
+      ++y0;
+    }
+    z0 += sz;
+    if (y0 >= ny) {
+      y0 -= ny;
+      ++z0;
     }
   }
   if (count > 0) {

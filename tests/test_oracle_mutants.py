@@ -130,3 +130,77 @@ def test_soft_sign_mutant_is_caught(monkeypatch):
     tau = np.array([0.25, 0.5, 0.75], np.float32)
     want = [pins._sig(10.0 * (float(t) - 0.5)) for t in tau]
     assert not np.allclose(oracle.ecc_soft(g, tau, 10.0), want)
+
+
+# ---------------------------------------------------- grid gradient mutants
+def _grad_mutant(kind):
+    """ecc_soft_bwd_grid with one planted mistake."""
+    def f(grid, tau, lam, grad_out):
+        grid, t, lam, g = oecc._grad_inputs(grid, tau, lam, grad_out)
+        X = grid.astype(np.float64)
+        index = np.arange(X.size).reshape(X.shape)
+        out = np.zeros(X.size)
+        for ext in itertools.product((0, 1), repeat=X.ndim):
+            anchors = [n - e for n, e in zip(X.shape, ext)]
+            if min(anchors) <= 0:
+                continue
+            offs = list(itertools.product(*[range(e + 1) for e in ext]))
+            if kind == "last_index_ties":
+                offs = offs[::-1]
+            vals = np.stack([X[tuple(slice(o, o + a) for o, a in zip(off, anchors))] for off in offs])
+            idxs = np.stack([index[tuple(slice(o, o + a) for o, a in zip(off, anchors))] for off in offs])
+            am = np.argmax(vals, axis=0)
+            v = np.take_along_axis(vals, am[None], 0)[0].ravel()
+            tgt = np.take_along_axis(idxs, am[None], 0)[0].ravel()
+            if kind == "to_anchor":
+                tgt = idxs[0].ravel()
+            sign = 1 if kind == "no_dim_sign" else (-1) ** sum(ext)
+            lam_f = 1.0 if kind == "no_lambda" else lam
+            pre = lam_f if kind == "plus_sign" else -lam_f
+            np.add.at(out, tgt, pre * sign * oecc._h_of(v, t, lam, g))
+        return out.reshape(X.shape)
+    return f
+
+
+def _run_grad_pins():
+    """Finite differences of the by-hand forward, the constant-grid closed form
+    and the sum rule; True if the current oracle.ecc_soft_bwd_grid passes all."""
+    rng = np.random.default_rng(4321)
+    lam = 9.0
+    tau = np.linspace(-0.1, 1.1, 7).astype(np.float32)
+    gout = rng.standard_normal(7).astype(np.float32)
+    for shape in ((3, 4), (2, 3, 3)):
+        n = int(np.prod(shape))
+        g = (rng.permutation(n) / n).reshape(shape)
+        got = oracle.ecc_soft_bwd_grid(g, tau, lam, gout)
+        h = 1e-6
+        for p in np.ndindex(*shape):
+            up, dn = g.copy(), g.copy()
+            up[p] += h
+            dn[p] -= h
+            fd = float(np.dot(gout.astype(np.float64),
+                              np.subtract(pins.soft_by_hand(up, tau, lam), pins.soft_by_hand(dn, tau, lam)))) / (2 * h)
+            if abs(fd - got[p]) > 1e-6 * max(1.0, abs(got[p])):
+                return False
+        c = np.full(shape, 0.5, np.float32)
+        want = np.zeros(shape)
+        want[tuple(s - 1 for s in shape)] = -lam * sum(
+            float(gk) * pins._sig(lam * (float(t) - 0.5)) * (1 - pins._sig(lam * (float(t) - 0.5)))
+            for t, gk in zip(tau, gout))
+        if not np.allclose(oracle.ecc_soft_bwd_grid(c, tau, lam, gout), want, rtol=1e-12, atol=1e-15):
+            return False
+        q = (rng.integers(0, 3, shape) / 2).astype(np.float32)
+        s = oracle.ecc_soft_bwd_grid(q, tau, lam, gout).sum()
+        if abs(s + oracle.ecc_soft_bwd_tau(q, tau, lam, gout).sum()) > 1e-9:
+            return False
+    return True
+
+
+def test_unpatched_grid_gradient_passes_pins():
+    assert _run_grad_pins()
+
+
+@pytest.mark.parametrize("kind", ["last_index_ties", "to_anchor", "no_dim_sign", "no_lambda", "plus_sign"])
+def test_grid_gradient_mutants_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(oracle, "ecc_soft_bwd_grid", _grad_mutant(kind))
+    assert not _run_grad_pins()
