@@ -10,8 +10,8 @@ an ECC entry point without the library raises ImportError.
 __version__ = "0.1.0"
 
 _API = (
-    "ecc_hard_2d", "ecc_hard_3d", "ecc_hard", "ecc_soft_fwd", "ecc_soft_bwd_tau",
-    "ecc_soft_bwd_grid", "workspace_bytes", "get_workspace", "EccError", "SoftECC", "soft_ecc",
+    "ecc_hard_2d", "ecc_hard_3d", "ecc_hard", "ecc_hard_batched", "ecc_soft_fwd", "ecc_soft_bwd_tau",
+    "ecc_soft_bwd_grid", "workspace_bytes", "workspace_bytes_batched", "get_workspace", "EccError", "SoftECC", "soft_ecc",
 )
 
 __all__ = list(_API)

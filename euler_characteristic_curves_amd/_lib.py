@@ -26,8 +26,9 @@ ECC_OP_SOFT_BWD = 2
 ECC_MAX_THRESHOLDS = 8192
 
 EXPORTS = (
-    "ecc_hard_2d", "ecc_hard_3d", "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
-    "ecc_workspace_bytes", "ecc_status_string", "ecc_last_error", "ecc_version",
+    "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
+    "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
+    "ecc_workspace_bytes", "ecc_workspace_bytes_batched", "ecc_status_string", "ecc_last_error", "ecc_version",
 )
 
 
@@ -51,6 +52,10 @@ def _load():
     lib.ecc_hard_2d.restype = I
     lib.ecc_hard_3d.argtypes = [P, I, I64, I64, I64, P, I32, P, P, SZ, P]
     lib.ecc_hard_3d.restype = I
+    lib.ecc_hard_2d_batched.argtypes = [P, I, I64, I64, I64, P, I64, I32, P, P, SZ, P]
+    lib.ecc_hard_2d_batched.restype = I
+    lib.ecc_hard_3d_batched.argtypes = [P, I, I64, I64, I64, I64, P, I64, I32, P, P, SZ, P]
+    lib.ecc_hard_3d_batched.restype = I
     lib.ecc_soft_fwd.argtypes = [P, I32, P, P, I32, F, P, P, SZ, P]
     lib.ecc_soft_fwd.restype = I
     lib.ecc_soft_bwd_tau.argtypes = [P, I32, P, P, I32, F, P, P, P, SZ, P]
@@ -59,6 +64,8 @@ def _load():
     lib.ecc_soft_bwd_grid.restype = I
     lib.ecc_workspace_bytes.argtypes = [I, I32, P, I32]
     lib.ecc_workspace_bytes.restype = SZ
+    lib.ecc_workspace_bytes_batched.argtypes = [I, I64, I32]
+    lib.ecc_workspace_bytes_batched.restype = SZ
     lib.ecc_status_string.argtypes = [I]
     lib.ecc_status_string.restype = ctypes.c_char_p
     lib.ecc_last_error.argtypes = []

@@ -26,8 +26,10 @@ int fail(int status, const char* fmt, const char* detail = nullptr, long long a 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
 
+// Per-grid checks of the hard entry points; the workspace is checked only
+// when `with_ws` (batched calls check it for the whole batch).
 int check_hard(const void* grid, int dtype, int64_t nz, int64_t ny, int64_t nx, const float* tau,
-               int32_t H, const int64_t* out, const void* ws, size_t ws_bytes) {
+               int32_t H, const int64_t* out, const void* ws, size_t ws_bytes, bool with_ws = true) {
   g_err[0] = 0;
   if (!grid) return fail(ECC_E_NULL, "%sgrid is NULL");
   if (!tau) return fail(ECC_E_NULL, "%stau is NULL");
@@ -40,8 +42,25 @@ int check_hard(const void* grid, int dtype, int64_t nz, int64_t ny, int64_t nx, 
     return fail(ECC_E_SHAPE, "%sgrid has more than 2^40 voxels");
   if (H < 1 || H > ECC_MAX_THRESHOLDS)
     return fail(ECC_E_NTHRESH, "%sH=%lld outside [1, %lld]", nullptr, H, ECC_MAX_THRESHOLDS);
+  if (!with_ws) return ECC_OK;
   if (!ws) return fail(ECC_E_WORKSPACE, "%sworkspace is NULL");
   const size_t need = ecc::workspace_bytes(H);
+  if (ws_bytes < need)
+    return fail(ECC_E_WORKSPACE, "%sworkspace has %lld bytes, needs %lld", nullptr, (long long)ws_bytes,
+                (long long)need);
+  return ECC_OK;
+}
+
+// Batch-specific checks: batch >= 1, tau_stride >= 0, all voxels within the
+// ABI limit, and (when `with_ws`) a workspace slice for every grid.
+int check_batch(int64_t batch, int64_t tau_stride, int64_t nvox, const void* ws, size_t ws_bytes,
+                int32_t H, bool with_ws) {
+  if (batch < 1) return fail(ECC_E_SHAPE, "%sbatch=%lld, must be >= 1", nullptr, batch);
+  if (tau_stride < 0) return fail(ECC_E_SHAPE, "%stau_stride=%lld, must be >= 0", nullptr, tau_stride);
+  if (batch > ECC_MAX_VOXELS / nvox) return fail(ECC_E_SHAPE, "%sbatch has more than 2^40 voxels");
+  if (!with_ws) return ECC_OK;
+  if (!ws) return fail(ECC_E_WORKSPACE, "%sworkspace is NULL");
+  const size_t need = (size_t)batch * ecc::batch_ws_stride(H, batch);
   if (ws_bytes < need)
     return fail(ECC_E_WORKSPACE, "%sworkspace has %lld bytes, needs %lld", nullptr, (long long)ws_bytes,
                 (long long)need);
@@ -124,6 +143,27 @@ int ecc_hard_3d(const void* grid, int dtype, int64_t nz, int64_t ny, int64_t nx,
   return hip_status(ecc::launch_hard(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int ecc_hard_2d_batched(const void* grid, int dtype, int64_t batch, int64_t ny, int64_t nx,
+                        const float* tau, int64_t tau_stride, int32_t H, int64_t* out, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return ecc_hard_3d_batched(grid, dtype, batch, 1, ny, nx, tau, tau_stride, H, out, ws, ws_bytes, stream);
+}
+
+int ecc_hard_3d_batched(const void* grid, int dtype, int64_t batch, int64_t nz, int64_t ny, int64_t nx,
+                        const float* tau, int64_t tau_stride, int32_t H, int64_t* out, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int st = check_hard(grid, dtype, nz, ny, nx, tau, H, out, ws, ws_bytes, false);
+  if (st != ECC_OK) return st;
+  st = check_batch(batch, tau_stride, nz * ny * nx, ws, ws_bytes, H, true);
+  if (st != ECC_OK) return st;
+  ecc::HardArgs a{grid, dtype, nz, ny, nx, tau, H, out, ws};
+  a.batch = batch;
+  a.tau_stride = tau_stride;
+  a.ws_stride = ecc::batch_ws_stride(H, batch);
+  a.acc_copies = ecc::batch_copies(batch);
+  return hip_status(ecc::launch_hard(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int ecc_soft_fwd(const float* grid, int32_t ndim, const int64_t* shape, const float* tau, int32_t H,
                  float lambda, float* out, void* ws, size_t ws_bytes, void* stream) {
   int64_t d[3];
@@ -160,6 +200,12 @@ size_t ecc_workspace_bytes(int op, int32_t ndim, const int64_t* shape, int32_t H
   if (op != ECC_OP_HARD && op != ECC_OP_SOFT_FWD && op != ECC_OP_SOFT_BWD) return 0;
   if (H < 1 || H > ECC_MAX_THRESHOLDS) return 0;
   return ecc::workspace_bytes(H);
+}
+
+size_t ecc_workspace_bytes_batched(int op, int64_t batch, int32_t H) {
+  if (op != ECC_OP_HARD && op != ECC_OP_SOFT_FWD && op != ECC_OP_SOFT_BWD) return 0;
+  if (H < 1 || H > ECC_MAX_THRESHOLDS || batch < 1 || batch > ECC_MAX_VOXELS) return 0;
+  return (size_t)batch * ecc::batch_ws_stride(H, batch);
 }
 
 const char* ecc_status_string(int status) {

@@ -35,7 +35,7 @@ __device__ __forceinline__ void agent_store(double* p, double v) {
 
 // Grid-wide reduction of per-workgroup rows of n int64 values, one launch.
 //
-// Every workgroup adds its non-zero values into one of kAccCopies int64
+// Every workgroup adds its non-zero values into one of `copies` int64
 // accumulator rows with device-scope atomic adds, waits until all of its own
 // memory operations are acknowledged, and only then takes a ticket.  On this
 // GPU, device-scope atomics are performed at the point of coherence shared by
@@ -48,11 +48,17 @@ __device__ __forceinline__ void agent_store(double* p, double v) {
 // accumulators and the ticket zero for the next launch.  Integer addition is
 // associative, so the totals do not depend on the order of arrival.
 template <int NT = kBlock, typename Local>
-__device__ bool grid_reduce(void* ws, int H, int n, Local local, long long* tot, int* lds_flag) {
+__device__ bool grid_reduce(void* ws, int H, int n, Local local, long long* tot, int* lds_flag,
+                            int copies = kAccCopies) {
+  if (gridDim.x == 1) {  // a lone workgroup holds the totals already (tot must not alias local's data)
+    for (int b = threadIdx.x; b < n; b += NT) tot[b] = local(b);
+    __syncthreads();
+    return true;
+  }
   unsigned int* ticket = reinterpret_cast<unsigned int*>(ws);
   long long* acc = reinterpret_cast<long long*>(reinterpret_cast<char*>(ws) + kWsHeader);
   const int stride = acc_bins(H);
-  long long* mine = acc + (size_t)(blockIdx.x % kAccCopies) * stride;
+  long long* mine = acc + (size_t)(blockIdx.x % copies) * stride;
   for (int b = threadIdx.x; b < n; b += NT) {
     const long long v = local(b);
     if (v != 0) __hip_atomic_fetch_add(mine + b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -70,11 +76,11 @@ __device__ bool grid_reduce(void* ws, int H, int n, Local local, long long* tot,
   for (int b = threadIdx.x; b < n; b += NT) {
     long long s = 0;
 #pragma unroll
-    for (int c = 0; c < kAccCopies; ++c) s += agent_load(acc + (size_t)c * stride + b);
+    for (int c = 0; c < copies; ++c) s += agent_load(acc + (size_t)c * stride + b);
     tot[b] = s;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kAccCopies * stride; i += NT) agent_store(acc + i, 0LL);
+  for (int i = threadIdx.x; i < copies * stride; i += NT) agent_store(acc + i, 0LL);
   return true;
 }
 

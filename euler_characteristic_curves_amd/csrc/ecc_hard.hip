@@ -177,7 +177,23 @@ __device__ __forceinline__ void flush_and_finish(const HardArgs& a, int nbins, i
     for (int c = 0; c < C; ++c) s += hist[b * C + c];
     return s;
   };
-  if (!grid_reduce<NT>(a.ws, a.H, nbins, local, tot, flag)) return;
+  if (gridDim.x == 1) {
+    // A lone workgroup: no device atomics.  tot aliases the histogram, and
+    // tot[b] covers the counters of bins near 2b/C: bins <= b for C >= 2,
+    // bins 2b and 2b+1 for C == 1.  Chunks of NT bins are read into
+    // registers and then written, bottom-up for C >= 2 and top-down for
+    // C == 1, so no counter is overwritten before it is read.
+    const int nch = (nbins + NT - 1) / NT;
+    for (int jj = 0; jj < nch; ++jj) {
+      const int b = (C >= 2 ? jj : nch - 1 - jj) * NT + (int)threadIdx.x;
+      const long long v = b < nbins ? local(b) : 0;
+      __syncthreads();
+      if (b < nbins) tot[b] = v;
+      __syncthreads();
+    }
+  } else if (!grid_reduce<NT>(a.ws, a.H, nbins, local, tot, flag, a.acc_copies)) {
+    return;
+  }
   int64_t* out = a.out;
   if constexpr (DT == 0) {
     // per-value histogram -> weighted count of values <= v
@@ -633,11 +649,22 @@ __device__ __forceinline__ Lds setup_lds(unsigned char* smem, const HardArgs& a,
   return L;
 }
 
+// The grid of a batch that this workgroup row works on.
+__device__ __forceinline__ void batch_slice(HardArgs& a) {
+  const int64_t b = blockIdx.y;
+  const size_t esz = a.dtype == 0 ? 1 : 4;
+  a.grid = reinterpret_cast<const char*>(a.grid) + (size_t)b * (size_t)(a.nz * a.ny * a.nx) * esz;
+  a.tau += b * a.tau_stride;
+  a.out += b * a.H;
+  a.ws = reinterpret_cast<char*>(a.ws) + (size_t)b * a.ws_stride;
+}
+
 template <int DT, int VEC, int C, int TH, int NT>
 __global__ __launch_bounds__(NT) void hard2d_kernel(HardArgs a, int nbins, int64_t ntx, int64_t ntiles,
                                                     int vec_ok, int th) {
   extern __shared__ __align__(16) unsigned char smem[];
   using T = typename Elem<DT>::T;
+  batch_slice(a);
   BinCtx bc;
   FastBin fb;
   LutBin lb;
@@ -961,6 +988,7 @@ __global__ __launch_bounds__(NT, MINW) void hard3d_kernel(HardArgs a, int nbins,
                                                           int vec_ok, int nlut) {
   extern __shared__ __align__(16) unsigned char smem[];
   using T = typename Elem<DT>::T;
+  batch_slice(a);
   BinCtx bc;
   FastBin fb;
   LutBin lb;
@@ -1114,13 +1142,39 @@ int copies_for(int dt, int nbins) {
   return 1;
 }
 
+// Workgroups per grid when `batch` grids share a launch that wants `total`.
+int64_t per_grid_blocks(int64_t total, int64_t batch) {
+  const int64_t g = (total + batch - 1) / batch;
+  return g < 1 ? 1 : g;
+}
+
+// Launch `go(args, nb)` for consecutive runs of at most kMaxBatchPerLaunch
+// grids, with the pointers moved to the run's first grid.
+template <typename Go>
+hipError_t launch_batches(const HardArgs& a, Go go) {
+  const size_t esz = a.dtype == 0 ? 1 : 4;
+  const size_t grid_bytes = (size_t)(a.nz * a.ny * a.nx) * esz;
+  for (int64_t b0 = 0; b0 < a.batch; b0 += kMaxBatchPerLaunch) {
+    const int64_t nb = a.batch - b0 < kMaxBatchPerLaunch ? a.batch - b0 : kMaxBatchPerLaunch;
+    HardArgs c = a;
+    c.grid = reinterpret_cast<const char*>(a.grid) + (size_t)b0 * grid_bytes;
+    c.tau = a.tau + b0 * a.tau_stride;
+    c.out = a.out + b0 * a.H;
+    c.ws = reinterpret_cast<char*>(a.ws) + (size_t)b0 * a.ws_stride;
+    go(c, (unsigned)nb);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int DT, int VEC, int C, int TH>
 hipError_t launch2d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInfo& di) {
   constexpr int64_t CHUNK = 64 * VEC;
   const int64_t ntx = (a.nx + CHUNK - 1) / CHUNK;
   // rows per wave: TH on large grids, fewer when that would leave the chip
   // short of workgroups (the per-wave row walk is serial)
-  int64_t want = (int64_t)di.cus * 4;
+  int64_t want = per_grid_blocks((int64_t)di.cus * 4, a.batch);
   {
     const int64_t u = useful_blocks(a.ny * a.nx, nbins, di.cus);
     if (want > u) want = u;
@@ -1143,8 +1197,9 @@ hipError_t launch2d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   if (g > want) g = want;
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
-  hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), lds, s, a, nbins, ntx, ntiles, vec_ok, (int)th);
-  return hipGetLastError();
+  return launch_batches(a, [&](const HardArgs& c, unsigned nb) {
+    hipLaunchKernelGGL(k, dim3((unsigned)g, nb), dim3(kBlock), lds, s, c, nbins, ntx, ntiles, vec_ok, (int)th);
+  });
 }
 
 template <int DT, int VEC, int C, int TY, int NT, int MINW>
@@ -1154,7 +1209,7 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   const int64_t ntx = (a.nx + CHUNK - 1) / CHUNK;
   const int64_t nty4 = (a.ny + TY * WAVES - 1) / (TY * WAVES);
   // split z so that there are enough tiles to fill the chip
-  int64_t want = (int64_t)di.cus * (4 * 256 / NT);
+  int64_t want = per_grid_blocks((int64_t)di.cus * (4 * 256 / NT), a.batch);
   {
     const int64_t u = useful_blocks(a.nz * a.ny * a.nx, nbins, di.cus);
     if (want > u) want = u;
@@ -1181,9 +1236,10 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   if (g > want) g = want;
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
-  hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(NT), lds, s, a, nbins, ntx, nty4, TZ, ntiles,
-                     vec_ok, nlut);
-  return hipGetLastError();
+  return launch_batches(a, [&](const HardArgs& c, unsigned nb) {
+    hipLaunchKernelGGL(k, dim3((unsigned)g, nb), dim3(NT), lds, s, c, nbins, ntx, nty4, TZ, ntiles,
+                       vec_ok, nlut);
+  });
 }
 
 template <int C>

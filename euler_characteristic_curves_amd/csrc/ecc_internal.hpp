@@ -10,20 +10,30 @@ namespace ecc {
 
 constexpr int kBlock = 256;        // threads per workgroup (4 waves of 64)
 constexpr int kWavesPerBlock = kBlock / 64;
-constexpr int kAccCopies = 8;      // global accumulator copies, picked by blockIdx % kAccCopies
+constexpr int kAccCopies = 8;      // global accumulator copies of one grid, picked by blockIdx % copies
 
 // Bins of the global accumulators: hard uint8 grids histogram their raw byte
 // value (256 keys), everything else threshold indices (H keys).
 __host__ __device__ inline int acc_bins(int H) { return H > 256 ? H : 256; }
 
-// Workspace: [ticket + padding | kAccCopies x acc_bins(H) int64 accumulators].
-// All of it must be zero between calls; the last workgroup of every launch
-// leaves it zero.
+// Workspace of one grid: [ticket + padding | copies x acc_bins(H) int64
+// accumulators].  All of it must be zero between calls; the last workgroup of
+// every launch leaves it zero.
 constexpr size_t kWsHeader = 256;
-inline size_t workspace_bytes(int H) {
-  return kWsHeader + (size_t)kAccCopies * (size_t)acc_bins(H) * sizeof(long long);
+inline size_t workspace_bytes(int H, int copies = kAccCopies) {
+  return kWsHeader + (size_t)copies * (size_t)acc_bins(H) * sizeof(long long);
 }
 
+// Accumulator copies per grid in a batch: the workgroups of a launch are
+// shared among the grids, so fewer of them flush into each grid's totals.
+inline int batch_copies(int64_t batch) {
+  return batch >= kAccCopies ? 1 : (int)(kAccCopies / batch);
+}
+
+// A batch of `batch` grids of one shape, stored back to back.  Grid b reads
+// tau + b * tau_stride (0: one threshold array for all), writes out + b * H and
+// uses the workspace at ws + b * ws_stride.  Workgroup row blockIdx.y of a
+// launch is grid blockIdx.y of the pointers it is given.
 struct HardArgs {
   const void* grid;
   int dtype;          // 0 = u8, 1 = f32
@@ -32,8 +42,13 @@ struct HardArgs {
   int H;
   int64_t* out;
   void* ws;
+  int64_t batch = 1;
+  int64_t tau_stride = 0;
+  size_t ws_stride = 0;
+  int acc_copies = kAccCopies;
 };
 
+// Batches as for HardArgs; grad_out of grid b is grad_out + b * H.
 struct SoftArgs {
   const float* grid;
   int64_t nz, ny, nx;  // nz = 1 for 2D
@@ -41,8 +56,12 @@ struct SoftArgs {
   int H;
   float lambda;
   const float* grad_out;  // null for the forward pass
-  float* out;             // S (forward) or grad_tau (backward)
+  float* out;             // S (forward) or grad_tau (backward), H per grid
   void* ws;
+  int64_t batch = 1;
+  int64_t tau_stride = 0;
+  size_t ws_stride = 0;
+  int acc_copies = kAccCopies;
 };
 
 struct GradArgs {
@@ -53,7 +72,17 @@ struct GradArgs {
   float lambda;
   const float* grad_out;
   float* out;  // grad_grid, one value per voxel
+  int64_t batch = 1;
+  int64_t tau_stride = 0;
 };
+
+// Largest number of grids in one launch (the workgroup grid's y extent).
+constexpr int64_t kMaxBatchPerLaunch = 65535;
+
+// Workspace stride between the grids of a batch.
+inline size_t batch_ws_stride(int H, int64_t batch) {
+  return (workspace_bytes(H, batch_copies(batch)) + 255) & ~(size_t)255;
+}
 
 struct DeviceInfo {
   int cus;

@@ -13,8 +13,8 @@ from . import _lib
 from ._lib import EccError, check, lib
 
 __all__ = [
-    "ecc_hard_2d", "ecc_hard_3d", "ecc_hard", "ecc_soft_fwd", "ecc_soft_bwd_tau",
-    "ecc_soft_bwd_grid", "workspace_bytes", "get_workspace", "EccError", "SoftECC", "soft_ecc",
+    "ecc_hard_2d", "ecc_hard_3d", "ecc_hard", "ecc_hard_batched", "ecc_soft_fwd", "ecc_soft_bwd_tau",
+    "ecc_soft_bwd_grid", "workspace_bytes", "workspace_bytes_batched", "get_workspace", "EccError", "SoftECC", "soft_ecc",
 ]
 
 _WS = {}
@@ -24,6 +24,13 @@ def workspace_bytes(op, H, shape=None):
     n = lib.ecc_workspace_bytes(op, len(shape) if shape else 0, None, int(H))
     if n == 0:
         raise EccError(_lib.ECC_E_NTHRESH, f"no workspace size for op={op} H={H}")
+    return int(n)
+
+
+def workspace_bytes_batched(op, batch, H):
+    n = lib.ecc_workspace_bytes_batched(op, int(batch), int(H))
+    if n == 0:
+        raise EccError(_lib.ECC_E_NTHRESH, f"no workspace size for op={op} batch={batch} H={H}")
     return int(n)
 
 
@@ -117,6 +124,42 @@ def ecc_hard(grid, tau, out=None, ws=None):
     if grid.dim() == 3:
         return ecc_hard_3d(grid, tau, out, ws)
     raise ValueError("grid must be 2D or 3D")
+
+
+def ecc_hard_batched(grids, tau, out=None, ws=None):
+    """Hard ECC of a batch of grids [B, ny, nx] or [B, nz, ny, nx]: int64[B, H].
+
+    ``tau`` is float32[H] (shared by every grid) or float32[B, H] (one row per
+    grid); see ecc_hard_2d_batched / ecc_hard_3d_batched in include/ecc.h.
+    """
+    _dev_tensor(grids, "grids")
+    if grids.dim() not in (3, 4):
+        raise ValueError("grids must be [B, ny, nx] or [B, nz, ny, nx]")
+    _dev_tensor(tau, "tau", torch.float32, grids.device)
+    B = grids.shape[0]
+    if tau.dim() == 1:
+        H, tau_stride = tau.numel(), 0
+    elif tau.dim() == 2 and tau.shape[0] == B:
+        H, tau_stride = tau.shape[1], tau.shape[1]
+    else:
+        raise ValueError("tau must be [H] or [B, H]")
+    if out is None:
+        out = torch.empty((B, H), dtype=torch.int64, device=grids.device)
+    _dev_tensor(out, "out", torch.int64, grids.device)
+    if tuple(out.shape) != (B, H):
+        raise ValueError("out must be [B, H]")
+    s = _stream(grids)
+    nb = workspace_bytes_batched(_lib.ECC_OP_HARD, B, H)
+    ws = get_workspace(nb, grids.device, s) if ws is None else ws
+    args = (_ptr(tau), tau_stride, H, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+            ctypes.c_void_p(s.cuda_stream))
+    if grids.dim() == 3:
+        check(lib.ecc_hard_2d_batched(_ptr(grids), _grid_dtype(grids), B, grids.shape[1], grids.shape[2], *args),
+              "ecc_hard_2d_batched")
+    else:
+        check(lib.ecc_hard_3d_batched(_ptr(grids), _grid_dtype(grids), B, grids.shape[1], grids.shape[2],
+                                      grids.shape[3], *args), "ecc_hard_3d_batched")
+    return out
 
 
 def _shape_arr(grid):

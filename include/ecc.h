@@ -54,7 +54,7 @@ extern "C" {
 /* status codes */
 #define ECC_OK 0
 #define ECC_E_NULL 1      /* a required pointer is NULL                      */
-#define ECC_E_SHAPE 2     /* ndim not 2/3, a dimension < 1, or too many voxels */
+#define ECC_E_SHAPE 2     /* ndim not 2/3, a dimension or batch < 1, tau_stride < 0, or too many voxels */
 #define ECC_E_DTYPE 3     /* dtype is not ECC_U8 / ECC_F32                    */
 #define ECC_E_NTHRESH 4   /* H < 1 or H > ECC_MAX_THRESHOLDS                  */
 #define ECC_E_LAMBDA 5    /* lambda not finite or <= 0                        */
@@ -98,6 +98,28 @@ int ecc_hard_2d(const void* grid, int dtype, int64_t ny, int64_t nx, const float
  */
 int ecc_hard_3d(const void* grid, int dtype, int64_t nz, int64_t ny, int64_t nx, const float* tau,
                 int32_t H, int64_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Hard ECC of a batch of `batch` 2D grids of one shape, stored back to back:
+ * grid[batch][ny][nx].  Grid b is binned against tau + b * tau_stride
+ * (tau_stride = 0: one float32[H] threshold array for every grid; H: one row
+ * of a float32[batch][H] array per grid) and its curve, defined as for
+ * ecc_hard_2d, goes to out[b][0..H) (int64[batch][H]).
+ *   ws  device workspace of ecc_workspace_bytes_batched(ECC_OP_HARD, batch, H)
+ *       bytes, zero-filled before first use, left zero-filled by every call.
+ * Batched execution is what the page lists as missing for training-scale use
+ * (section "Limitations and outlook"): one small grid cannot fill the GPU, a
+ * batch can.  Each grid gets its own workgroups, so the result equals that of
+ * `batch` separate calls, bit for bit.  One kernel launch per 65535 grids.
+ */
+int ecc_hard_2d_batched(const void* grid, int dtype, int64_t batch, int64_t ny, int64_t nx,
+                        const float* tau, int64_t tau_stride, int32_t H, int64_t* out, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Batched hard ECC of 3D grids grid[batch][nz][ny][nx]; otherwise as ecc_hard_2d_batched. */
+int ecc_hard_3d_batched(const void* grid, int dtype, int64_t batch, int64_t nz, int64_t ny, int64_t nx,
+                        const float* tau, int64_t tau_stride, int32_t H, int64_t* out, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /*
  * Soft ECC forward (differentiable ECC layer).
@@ -153,6 +175,12 @@ int ecc_soft_bwd_grid(const float* grid, int32_t ndim, const int64_t* shape, con
  * it today) and H thresholds.  Returns 0 for invalid op/H.
  */
 size_t ecc_workspace_bytes(int op, int32_t ndim, const int64_t* shape, int32_t H);
+
+/*
+ * Bytes of workspace for a batched operation (ECC_OP_*) over `batch` grids
+ * with H thresholds: one slice per grid.  Returns 0 for invalid arguments.
+ */
+size_t ecc_workspace_bytes_batched(int op, int64_t batch, int32_t H);
 
 /* Static text for a status code (never NULL). */
 const char* ecc_status_string(int status);

@@ -38,6 +38,7 @@ from .ecc import (  # noqa: F401
     cell_counts,
     first_k_bins,
     ecc_hard,
+    ecc_hard_batched,
     ecc_at,
     ecc_at_many,
     ecc_soft,

@@ -27,7 +27,7 @@ __all__ = [
     "cell_values", "cell_counts", "first_k_bins", "ecc_hard", "ecc_at",
     "sigmoid", "ecc_soft", "ecc_soft_percell", "ecc_soft_at",
     "ecc_soft_bwd_tau", "ecc_soft_bwd_at", "ecc_at_many", "ecc_soft_at_many",
-    "ecc_soft_bwd_at_many", "ecc_soft_bwd_grid", "ecc_soft_bwd_grid_at",
+    "ecc_soft_bwd_at_many", "ecc_soft_bwd_grid", "ecc_soft_bwd_grid_at", "ecc_hard_batched",
 ]
 
 
@@ -402,3 +402,20 @@ def ecc_soft_bwd_grid_at(grid, points, tau, lam, grad_out):
         h = float(_h_of(np.array([X[p]]), t, lam, g)[0]) if c else 0.0
         res.append(-lam * c * h)
     return np.array(res, dtype=np.float64)
+
+
+# ------------------------------------------------------------------ batches
+def ecc_hard_batched(grids, tau):
+    """Hard ECC of each grid of a batch: int64[B, H].
+
+    A batch is a set of independent grids (the page lists batched execution
+    among its next steps, section "Limitations and outlook"); no cell joins two
+    grids.  ``tau`` is one threshold array for all grids ([H]) or one row per
+    grid ([B, H]).  Written as the loop it is.
+    """
+    grids = np.asarray(grids)
+    tau = np.asarray(tau)
+    if grids.ndim not in (3, 4):
+        raise ValueError("grids must be [B, ny, nx] or [B, nz, ny, nx]")
+    rows = [ecc_hard(grids[b], tau if tau.ndim == 1 else tau[b]) for b in range(grids.shape[0])]
+    return np.stack(rows)

@@ -26,8 +26,10 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
-        "ecc_hard_2d", "ecc_hard_3d", "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
-        "ecc_workspace_bytes", "ecc_status_string", "ecc_last_error", "ecc_version"])
+        "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
+        "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
+        "ecc_workspace_bytes", "ecc_workspace_bytes_batched", "ecc_status_string", "ecc_last_error",
+        "ecc_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -63,6 +65,16 @@ def test_workspace_bytes(L):
     assert f(0, 3, None, 8192) % 8 == 0
 
 
+def test_workspace_bytes_batched(L):
+    f = L.lib.ecc_workspace_bytes_batched
+    assert f(0, 0, 16) == 0 and f(0, 1, 0) == 0 and f(9, 1, 16) == 0
+    one = f(0, 1, 256)
+    assert one >= L.lib.ecc_workspace_bytes(0, 2, None, 256) and one % 256 == 0
+    # grids of a large batch share the launch's workgroups: smaller slices
+    assert f(0, 1000, 256) < 1000 * one
+    assert f(0, 1000, 256) % 1000 == 0
+
+
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 
@@ -89,6 +101,28 @@ def test_hard_argument_errors(L):
     assert r == L.ECC_E_SHAPE
     r = L.lib.ecc_hard_3d(FAKE, 0, 1 << 14, 1 << 14, 1 << 14, FAKE, 4, FAKE, FAKE, 1 << 30, None)
     assert r == L.ECC_E_SHAPE
+
+
+def hard_batched(L, B=3, nz=2, ny=4, nx=4, tau_stride=0, H=4, grid=FAKE, tau=FAKE, out=FAKE, ws=FAKE,
+                 wsb=1 << 40, dtype=1):
+    return L.lib.ecc_hard_3d_batched(grid, dtype, B, nz, ny, nx, tau, tau_stride, H, out, ws, wsb, None)
+
+
+def test_hard_batched_argument_errors(L):
+    assert hard_batched(L, grid=None) == L.ECC_E_NULL
+    assert hard_batched(L, out=None) == L.ECC_E_NULL
+    assert hard_batched(L, dtype=5) == L.ECC_E_DTYPE
+    assert hard_batched(L, B=0) == L.ECC_E_SHAPE
+    assert b"batch" in L.lib.ecc_last_error()
+    assert hard_batched(L, B=-2) == L.ECC_E_SHAPE
+    assert hard_batched(L, tau_stride=-1) == L.ECC_E_SHAPE
+    assert hard_batched(L, nz=0) == L.ECC_E_SHAPE
+    assert hard_batched(L, B=1 << 30, nz=1 << 6, ny=1 << 6, nx=1 << 6) == L.ECC_E_SHAPE
+    assert hard_batched(L, H=0) == L.ECC_E_NTHRESH
+    assert hard_batched(L, ws=None) == L.ECC_E_WORKSPACE
+    need = L.lib.ecc_workspace_bytes_batched(0, 3, 4)
+    assert hard_batched(L, wsb=need - 1) == L.ECC_E_WORKSPACE
+    assert L.lib.ecc_hard_2d_batched(FAKE, 1, 0, 4, 4, FAKE, 0, 4, FAKE, FAKE, 1 << 40, None) == L.ECC_E_SHAPE
 
 
 def soft(L, ndim=3, shape=(4, 4, 4), lam=1.0, H=4, grid=FAKE, tau=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30,

@@ -401,3 +401,22 @@ def test_oracle_rejects_bad_input():
     with pytest.raises(ValueError):
         oracle.ecc_soft(np.zeros((2, 2)), [0.0], float("nan"))
     assert oecc.first_k_bins(np.array([0.5, 2.0, -1.0]), [0.0, 1.0]).tolist() == [1, 2, 0]
+
+
+def test_batched_oracle_is_per_grid():
+    """A batch is independent grids: each row equals the grid's own curve, and
+    a batch stacked along a new axis is not the 3D grid of that stack."""
+    rng = np.random.default_rng(97)
+    g = rng.integers(0, 4, (5, 6, 7)).astype(np.float32)
+    tau = np.array([0, 1, 2, 3], np.float32)
+    rows = oracle.ecc_hard_batched(g, tau)
+    assert rows.shape == (5, 4)
+    for b in range(5):
+        assert rows[b].tolist() == [pins.brute_chi(g[b], float(t)) for t in tau]
+    per = np.stack([tau + 0.5 * b for b in range(5)]).astype(np.float32)
+    rows = oracle.ecc_hard_batched(g, per)
+    for b in range(5):
+        assert rows[b].tolist() == [pins.brute_chi(g[b], float(t)) for t in per[b]]
+    # all grids at their max: each contributes 1, while the 3D stack is one box (also 1),
+    # but below the max the 3D stack joins grids through z-edges
+    assert not np.array_equal(oracle.ecc_hard_batched(g, tau).sum(0), oracle.ecc_hard(g, tau))
