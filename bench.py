@@ -10,7 +10,8 @@ steps cannot be served from the 256 MB Infinity Cache.
 Also reported on the same JSON line: per-kernel durations (mean of
 back-to-back launches, and min / median of individually timed launches, HIP
 events on the launch stream) and the roofline of each hard kernel; the other
-grid sizes (128^2, 1024^2, 1024^3) as context; the soft forward and its
+grid sizes (128^2, 1024^2, 1024^3) as context, the first two also as batches
+of 1024 and 64 grids in one call; the soft forward and its
 backward with respect to the thresholds and to the grid at 256^3 (H=256,
 lambda=50) with their VALU-issue fraction; and the CPU oracle
 timed on a bounded sample of the same workloads (cpu_baseline), on one core
@@ -352,6 +353,22 @@ def main():
             context[name] = {"shape": list(dg.shape), "H": int(dtau.numel()), "ms": ms, "min_ms": mn,
                              "median_ms": md, "voxels_per_s": dg.numel() / (ms * 1e-3),
                              "GB_s": (dg.numel() * dg.element_size() + 12 * dtau.numel()) / (ms * 1e-3) / 1e9}
+            if name != "c4b_1024cube_f32":
+                # the same grid size as a batch: B distinct grids (rolled copies of
+                # this one), one call, one curve per grid
+                B = 1024 if name == "c1_128sq_f32" else 64
+                log("context batched", name, B)
+                gb = torch.stack([torch.roll(dg, shifts=(7 * b, 13 * b), dims=(0, 1)) for b in range(B)])
+                ob = torch.empty((B, dtau.numel()), dtype=torch.int64, device=dev)
+                fb = lambda i: E.ecc_hard_batched(gb, dtau, out=ob)
+                fb(0)
+                msb = timed(torch, fb, args.kernel_reps)
+                context[name]["batched"] = {
+                    "batch": B, "ms": msb, "us_per_grid": msb * 1e3 / B,
+                    "voxels_per_s": gb.numel() / (msb * 1e-3),
+                    "GB_s": (gb.numel() * gb.element_size() + 12 * dtau.numel()) / (msb * 1e-3) / 1e9,
+                    "speedup_per_grid_vs_single_calls": ms * B / msb}
+                del gb, ob
             del dg, dtau, o
             torch.cuda.empty_cache()
 

@@ -362,13 +362,17 @@ __device__ __forceinline__ void row2d(const int (&cur)[VEC], int cl, int cr, con
                          hist, lofs);
 }
 
-// Interior wave tile (aligned rows, column chunk inside the grid).  Rows
-// ys..ye-1 are processed, row ye is the halo.  Four rows of loads are in
-// flight: the row loop is unrolled by 4 so every load lands in a register
-// that is consumed in place (a register copy of an in-flight load would force
-// the wave to wait for it).  Rows past the grid are loaded from the last row
-// (always a valid address) and turned into trash keys.
-template <int DT, int VEC, int C>
+// Wave tile of aligned rows.  Rows ys..ye-1 are processed, row ye is the
+// halo.  Four rows of loads are in flight: the row loop is unrolled by 4 so
+// every load lands in a register that is consumed in place (a register copy
+// of an in-flight load would force the wave to wait for it).  Rows past the
+// grid are loaded from the last row (always a valid address) and turned into
+// trash keys.  PARTIAL: the column chunk runs past the row end (narrow grids,
+// the last chunk of a row).  Aligned rows hold a whole number of lane
+// vectors, so a lane is wholly inside or wholly past the row; lanes past it
+// load the chunk's first vector and carry trash keys, which also makes them
+// the out-of-grid right neighbour of the last real column.
+template <int DT, int VEC, int C, bool PARTIAL = false>
 __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, int64_t ny, int64_t nx,
                                             int64_t ys, int64_t ye, int64_t xb, int lane, int lofs,
                                             int* hist, int trash, const FastBin& fb) {
@@ -388,18 +392,20 @@ __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, in
   };
   const bool has_l = xb > 0, has_r = xb + CHUNK < nx;
   const int64_t xl = has_l ? xb - 1 : xb, xr = has_r ? xb + CHUNK : xb;
+  const bool lane_in = !PARTIAL || xb + (int64_t)lane * VEC < nx;
+  const int vlane = lane_in ? lane : 0;  // lanes past the row end load a valid vector
   const T* lastrow = grid + (ny - 1) * nx;
   auto rowp = [&](int64_t y) { return y < ny ? grid + y * nx : lastrow; };
   RawRow<DT, VEC> q0, q1, q2, q3;
   int cur[VEC], cl, cr;
   {
     RawRow<DT, VEC> r0;
-    fetch_row<DT, VEC>(r0, rowp(ys), xb, lane, xl, xr);
-    fetch_row<DT, VEC>(q0, rowp(ys + 1), xb, lane, xl, xr);
-    fetch_row<DT, VEC>(q1, rowp(ys + 2), xb, lane, xl, xr);
-    fetch_row<DT, VEC>(q2, rowp(ys + 3), xb, lane, xl, xr);
-    fetch_row<DT, VEC>(q3, rowp(ys + 4), xb, lane, xl, xr);
-    row_keys<DT, VEC>(r0, true, has_l, has_r, trash, fb, cur, cl, cr);
+    fetch_row<DT, VEC>(r0, rowp(ys), xb, vlane, xl, xr);
+    fetch_row<DT, VEC>(q0, rowp(ys + 1), xb, vlane, xl, xr);
+    fetch_row<DT, VEC>(q1, rowp(ys + 2), xb, vlane, xl, xr);
+    fetch_row<DT, VEC>(q2, rowp(ys + 3), xb, vlane, xl, xr);
+    fetch_row<DT, VEC>(q3, rowp(ys + 4), xb, vlane, xl, xr);
+    row_keys<DT, VEC>(r0, lane_in, has_l, has_r, trash, fb, cur, cl, cr);
     to_addr(cur, cl, cr);
   }
   int nxt[VEC], nl, nr;
@@ -407,9 +413,9 @@ __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, in
   // stage issued four rows ahead
 #define ECC_ROW2D_FAST(Q, K)                                                         \
   {                                                                                  \
-    row_keys<DT, VEC, false>(Q, true, has_l, has_r, trash, fb, nxt, nl, nr);         \
+    row_keys<DT, VEC, PARTIAL>(Q, lane_in, has_l, has_r, trash, fb, nxt, nl, nr);    \
     to_addr(nxt, nl, nr);                                                            \
-    fetch_row<DT, VEC>(Q, rowp(y + K + 5), xb, lane, xl, xr);                        \
+    fetch_row<DT, VEC>(Q, rowp(y + K + 5), xb, vlane, xl, xr);                       \
     row2d<VEC, C, ADDR>(cur, cl, cr, nxt, nl, nr, hist, lofs);                       \
     _Pragma("unroll") for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];                 \
     cl = nl;                                                                         \
@@ -418,7 +424,7 @@ __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, in
   // remainder: at most four rows, checked against the tile and grid ends
 #define ECC_ROW2D_TAIL(Q, K)                                                         \
   if (y + K < ye) {                                                                  \
-    row_keys<DT, VEC, true>(Q, y + K + 1 < ny, has_l, has_r, trash, fb, nxt, nl, nr); \
+    row_keys<DT, VEC, true>(Q, lane_in && y + K + 1 < ny, has_l, has_r, trash, fb, nxt, nl, nr); \
     to_addr(nxt, nl, nr);                                                            \
     row2d<VEC, C, ADDR>(cur, cl, cr, nxt, nl, nr, hist, lofs);                       \
     _Pragma("unroll") for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];                 \
@@ -690,6 +696,8 @@ __global__ __launch_bounds__(NT) void hard2d_kernel(HardArgs a, int nbins, int64
       const int64_t xb = tx * CHUNK;
       if (vok && xb + CHUNK <= nx)
         tile2d_fast<DT, VEC, C>(grid, ny, nx, ys, ye, xb, lane, lofs, L.hist, nbins, fb);
+      else if (vok)
+        tile2d_fast<DT, VEC, C, true>(grid, ny, nx, ys, ye, xb, lane, lofs, L.hist, nbins, fb);
       else
         tile2d_generic<DT, VEC, C>(grid, ny, nx, ys, ye, xb, lane, lofs, L.hist, vok, bc);
     }

@@ -77,6 +77,27 @@ def test_hard_random_shapes(E, shape, dtype):
         _check_hard(E, g, _taus(rng, g, H, kind), f"{dtype}-{kind}")
 
 
+@pytest.mark.parametrize("nx", [4, 16, 32, 64, 124, 128, 252, 260, 528, 1008, 1040, 1552])
+@pytest.mark.parametrize("dtype", ["u8", "f32", "f32ties"])
+def test_hard_aligned_partial_chunks(E, nx, dtype):
+    """Aligned rows whose last column chunk ends inside the row (narrow grids,
+    ragged right edges): lanes past the row end carry no cells."""
+    if dtype == "u8" and nx % 16:
+        nx = nx + (16 - nx % 16)  # keep u8 rows 16-byte aligned too
+    rng = np.random.default_rng(zlib.crc32(repr(("partial", nx, dtype)).encode()))
+    for ny in (1, 2, 7, 130):
+        if dtype == "u8":
+            g = rng.integers(0, 256, size=(ny, nx), dtype=np.uint8)
+            tau = W.tau_integers(256)
+        elif dtype == "f32":
+            g = rng.random((ny, nx), dtype=np.float32)
+            tau = W.tau_linspace(0.0, 1.0, 300)
+        else:
+            g = rng.integers(0, 4, size=(ny, nx)).astype(np.float32)
+            tau = np.array([-1, 0, 0.5, 1, 2, 3, 4], np.float32)
+        _check_hard(E, g, tau, f"partial-{dtype}-{ny}x{nx}")
+
+
 @pytest.mark.parametrize("H", [1, 3, 511, 512, 513, 2048, 4096, 8192])
 def test_hard_threshold_counts(E, H):
     rng = np.random.default_rng(H)
