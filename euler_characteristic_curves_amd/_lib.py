@@ -28,6 +28,7 @@ ECC_MAX_THRESHOLDS = 8192
 EXPORTS = (
     "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
     "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
+    "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_grid_batched",
     "ecc_workspace_bytes", "ecc_workspace_bytes_batched", "ecc_status_string", "ecc_last_error", "ecc_version",
 )
 
@@ -62,6 +63,12 @@ def _load():
     lib.ecc_soft_bwd_tau.restype = I
     lib.ecc_soft_bwd_grid.argtypes = [P, I32, P, P, I32, F, P, P, P]
     lib.ecc_soft_bwd_grid.restype = I
+    lib.ecc_soft_fwd_batched.argtypes = [P, I32, P, I64, P, I64, I32, F, P, P, SZ, P]
+    lib.ecc_soft_fwd_batched.restype = I
+    lib.ecc_soft_bwd_tau_batched.argtypes = [P, I32, P, I64, P, I64, I32, F, P, P, P, SZ, P]
+    lib.ecc_soft_bwd_tau_batched.restype = I
+    lib.ecc_soft_bwd_grid_batched.argtypes = [P, I32, P, I64, P, I64, I32, F, P, P, P]
+    lib.ecc_soft_bwd_grid_batched.restype = I
     lib.ecc_workspace_bytes.argtypes = [I, I32, P, I32]
     lib.ecc_workspace_bytes.restype = SZ
     lib.ecc_workspace_bytes_batched.argtypes = [I, I64, I32]

@@ -194,6 +194,55 @@ int ecc_soft_bwd_grid(const float* grid, int32_t ndim, const int64_t* shape, con
   return hip_status(ecc::launch_soft_grad(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int ecc_soft_fwd_batched(const float* grid, int32_t ndim, const int64_t* shape, int64_t batch,
+                         const float* tau, int64_t tau_stride, int32_t H, float lambda, float* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  int64_t d[3];
+  int st = check_soft(grid, ndim, shape, tau, H, lambda, out, ws, ws_bytes, d, false);
+  if (st != ECC_OK) return st;
+  st = check_batch(batch, tau_stride, d[0] * d[1] * d[2], ws, ws_bytes, H, true);
+  if (st != ECC_OK) return st;
+  ecc::SoftArgs a{grid, d[0], d[1], d[2], tau, H, lambda, nullptr, out, ws};
+  a.batch = batch;
+  a.tau_stride = tau_stride;
+  a.ws_stride = ecc::batch_ws_stride(H, batch);
+  a.acc_copies = ecc::batch_copies(batch);
+  return hip_status(ecc::launch_soft(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int ecc_soft_bwd_tau_batched(const float* grid, int32_t ndim, const int64_t* shape, int64_t batch,
+                             const float* tau, int64_t tau_stride, int32_t H, float lambda,
+                             const float* grad_out, float* grad_tau, void* ws, size_t ws_bytes,
+                             void* stream) {
+  int64_t d[3];
+  int st = check_soft(grid, ndim, shape, tau, H, lambda, grad_tau, ws, ws_bytes, d, false);
+  if (st != ECC_OK) return st;
+  if (!grad_out) return fail(ECC_E_NULL, "%sgrad_out is NULL");
+  st = check_batch(batch, tau_stride, d[0] * d[1] * d[2], ws, ws_bytes, H, true);
+  if (st != ECC_OK) return st;
+  ecc::SoftArgs a{grid, d[0], d[1], d[2], tau, H, lambda, grad_out, grad_tau, ws};
+  a.batch = batch;
+  a.tau_stride = tau_stride;
+  a.ws_stride = ecc::batch_ws_stride(H, batch);
+  a.acc_copies = ecc::batch_copies(batch);
+  return hip_status(ecc::launch_soft(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int ecc_soft_bwd_grid_batched(const float* grid, int32_t ndim, const int64_t* shape, int64_t batch,
+                              const float* tau, int64_t tau_stride, int32_t H, float lambda,
+                              const float* grad_out, float* grad_grid, void* stream) {
+  int64_t d[3];
+  int st = check_soft(grid, ndim, shape, tau, H, lambda, grad_grid, nullptr, 0, d, false);
+  if (st != ECC_OK) return st;
+  if (!grad_out) return fail(ECC_E_NULL, "%sgrad_out is NULL");
+  st = check_batch(batch, tau_stride, d[0] * d[1] * d[2], nullptr, 0, H, false);
+  if (st != ECC_OK) return st;
+  ecc::GradArgs a{grid, d[0], d[1], d[2], tau, H, lambda, grad_out, grad_grid};
+  a.batch = batch;
+  a.tau_stride = tau_stride;
+  return hip_status(ecc::launch_soft_grad(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t ecc_workspace_bytes(int op, int32_t ndim, const int64_t* shape, int32_t H) {
   (void)ndim;
   (void)shape;

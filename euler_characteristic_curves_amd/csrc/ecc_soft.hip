@@ -45,6 +45,14 @@ struct Term {
 template <bool BWD>
 __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles, int fx_shift) {
   extern __shared__ __align__(16) unsigned char smem[];
+  {  // the grid of a batch that this workgroup row works on
+    const int64_t b = blockIdx.y;
+    p.grid += b * (p.nz * p.ny * p.nx);
+    p.tau += b * p.tau_stride;
+    p.out += b * p.H;
+    if (BWD) p.grad_out += b * p.H;
+    p.ws = reinterpret_cast<char*>(p.ws) + (size_t)b * p.ws_stride;
+  }
   long long* tmp = reinterpret_cast<long long*>(smem);                 // 256
   int* misc = reinterpret_cast<int*>(tmp + kBlock);                    // [0]=count [1]=flag
   Term* terms = reinterpret_cast<Term*>(misc + 4);                     // kTermCap
@@ -228,7 +236,9 @@ __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles
   __syncthreads();
   const double scale = ldexp(1.0, fx_shift);
   long long* tot = reinterpret_cast<long long*>(terms);  // the term list is no longer needed
-  if (!grid_reduce(p.ws, H, H, [&](int k) { return __double2ll_rn(accS[k] * scale); }, tot, &misc[1])) return;
+  if (!grid_reduce(p.ws, H, H, [&](int k) { return __double2ll_rn(accS[k] * scale); }, tot, &misc[1],
+                   p.acc_copies))
+    return;
   const double inv = ldexp(1.0, -fx_shift);
   for (int k = tid; k < H; k += kBlock) {
     double v = (double)tot[k] * inv;
@@ -245,7 +255,8 @@ hipError_t launch_soft(const SoftArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int64_t nvox = a.nz * a.ny * a.nx;
   const int64_t ntiles = (nvox + kTileVox - 1) / kTileVox;
-  int64_t g = (int64_t)di.cus * 4;
+  // workgroups per grid: the launch's share of four per CU
+  int64_t g = ((int64_t)di.cus * 4 + a.batch - 1) / a.batch;
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
   // fixed point: |partial| and |total| <= #cells <= 8 * nvox, kept below 2^61
@@ -255,24 +266,26 @@ hipError_t launch_soft(const SoftArgs& a, hipStream_t s) {
   if (shift > 40) shift = 40;
   const size_t lds = kBlock * sizeof(long long) + 4 * sizeof(int) + kTermCap * sizeof(Term) +
                      (size_t)a.H * sizeof(double);
-  if (a.grad_out) {
-    auto k = soft_kernel<true>;
-    if (lds > 64 * 1024) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), lds, s, a, ntiles, shift);
-  } else {
-    auto k = soft_kernel<false>;
-    if (lds > 64 * 1024) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kBlock), lds, s, a, ntiles, shift);
+  auto k = a.grad_out ? soft_kernel<true> : soft_kernel<false>;
+  if (lds > 64 * 1024) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds);
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  // one launch per run of at most kMaxBatchPerLaunch grids
+  for (int64_t b0 = 0; b0 < a.batch; b0 += kMaxBatchPerLaunch) {
+    const int64_t nb = a.batch - b0 < kMaxBatchPerLaunch ? a.batch - b0 : kMaxBatchPerLaunch;
+    SoftArgs c = a;
+    c.grid = a.grid + b0 * nvox;
+    c.tau = a.tau + b0 * a.tau_stride;
+    c.out = a.out + b0 * a.H;
+    if (a.grad_out) c.grad_out = a.grad_out + b0 * a.H;
+    c.ws = reinterpret_cast<char*>(a.ws) + (size_t)b0 * a.ws_stride;
+    hipLaunchKernelGGL(k, dim3((unsigned)g, (unsigned)nb), dim3(kBlock), lds, s, c, ntiles, shift);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace ecc

@@ -135,6 +135,13 @@ __device__ __forceinline__ int64_t div_near(int64_t t, int64_t n, int64_t* rem) 
 template <bool D3>
 __global__ __launch_bounds__(kGradNT) void soft_grad_kernel(GradArgs p, int64_t nseg) {
   extern __shared__ __align__(16) unsigned char smem[];
+  {  // the grid of a batch that this workgroup row works on
+    const int64_t b = blockIdx.y, nv = p.nz * p.ny * p.nx;
+    p.grid += b * nv;
+    p.out += b * nv;
+    p.tau += b * p.tau_stride;
+    p.grad_out += b * p.H;
+  }
   QEntry* queues = reinterpret_cast<QEntry*>(smem);                     // kGradWaves x kQueueCap
   float2* T = reinterpret_cast<float2*>(queues + kGradWaves * kQueueCap);
   float* red = reinterpret_cast<float*>(smem);                          // setup only, 3 x kGradNT
@@ -315,12 +322,24 @@ hipError_t launch_grad(const GradArgs& a, hipStream_t s, int64_t nseg, const Dev
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), kGradNT, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
-  int64_t g = (int64_t)di.cus * per_cu;
+  // workgroups per grid: the launch's share of what fits on the chip
+  int64_t g = ((int64_t)di.cus * per_cu + a.batch - 1) / a.batch;
   const int64_t need = (nseg + kGradWaves - 1) / kGradWaves;
   if (g > need) g = need;
   if (g < 1) g = 1;
-  hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(kGradNT), lds, s, a, nseg);
-  return hipGetLastError();
+  const int64_t nvox = a.nz * a.ny * a.nx;
+  for (int64_t b0 = 0; b0 < a.batch; b0 += kMaxBatchPerLaunch) {
+    const int64_t nb = a.batch - b0 < kMaxBatchPerLaunch ? a.batch - b0 : kMaxBatchPerLaunch;
+    GradArgs c = a;
+    c.grid = a.grid + b0 * nvox;
+    c.out = a.out + b0 * nvox;
+    c.tau = a.tau + b0 * a.tau_stride;
+    c.grad_out = a.grad_out + b0 * a.H;
+    hipLaunchKernelGGL(k, dim3((unsigned)g, (unsigned)nb), dim3(kGradNT), lds, s, c, nseg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace

@@ -14,7 +14,8 @@ from ._lib import EccError, check, lib
 
 __all__ = [
     "ecc_hard_2d", "ecc_hard_3d", "ecc_hard", "ecc_hard_batched", "ecc_soft_fwd", "ecc_soft_bwd_tau",
-    "ecc_soft_bwd_grid", "workspace_bytes", "workspace_bytes_batched", "get_workspace", "EccError", "SoftECC", "soft_ecc",
+    "ecc_soft_bwd_grid", "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_grid_batched",
+    "workspace_bytes", "workspace_bytes_batched", "get_workspace", "EccError", "SoftECC", "soft_ecc",
 ]
 
 _WS = {}
@@ -252,3 +253,108 @@ class SoftECC(torch.autograd.Function):
 def soft_ecc(grid, tau, lam):
     """Soft ECC as an autograd op (differentiable in the grid and in tau)."""
     return SoftECC.apply(grid, tau, lam)
+
+
+# ------------------------------------------------------------ soft batches
+def _batch_args(grids, tau):
+    _dev_tensor(grids, "grids", torch.float32)
+    if grids.dim() not in (3, 4):
+        raise ValueError("grids must be [B, ny, nx] or [B, nz, ny, nx]")
+    _dev_tensor(tau, "tau", torch.float32, grids.device)
+    B = grids.shape[0]
+    if tau.dim() == 1:
+        H, tau_stride = tau.numel(), 0
+    elif tau.dim() == 2 and tau.shape[0] == B:
+        H, tau_stride = tau.shape[1], tau.shape[1]
+    else:
+        raise ValueError("tau must be [H] or [B, H]")
+    shp = (ctypes.c_int64 * (grids.dim() - 1))(*grids.shape[1:])
+    return B, H, tau_stride, shp
+
+
+def ecc_soft_fwd_batched(grids, tau, lam, out=None, ws=None):
+    """Soft ECC of each grid of a batch: float32[B, H] (see include/ecc.h)."""
+    B, H, ts, shp = _batch_args(grids, tau)
+    if out is None:
+        out = torch.empty((B, H), dtype=torch.float32, device=grids.device)
+    _dev_tensor(out, "out", torch.float32, grids.device)
+    if tuple(out.shape) != (B, H):
+        raise ValueError("out must be [B, H]")
+    s = _stream(grids)
+    nb = workspace_bytes_batched(_lib.ECC_OP_SOFT_FWD, B, H)
+    ws = get_workspace(nb, grids.device, s) if ws is None else ws
+    check(lib.ecc_soft_fwd_batched(_ptr(grids), grids.dim() - 1, ctypes.cast(shp, ctypes.c_void_p), B,
+                                   _ptr(tau), ts, H, float(lam), _ptr(out), _ptr(ws),
+                                   ws.numel() * ws.element_size(), ctypes.c_void_p(s.cuda_stream)),
+          "ecc_soft_fwd_batched")
+    return out
+
+
+def ecc_soft_bwd_tau_batched(grids, tau, lam, grad_out, grad_tau=None, ws=None):
+    """Per-grid dL/dtau of a batch, float32[B, H] (see include/ecc.h)."""
+    B, H, ts, shp = _batch_args(grids, tau)
+    _dev_tensor(grad_out, "grad_out", torch.float32, grids.device)
+    if tuple(grad_out.shape) != (B, H):
+        raise ValueError("grad_out must be [B, H]")
+    if grad_tau is None:
+        grad_tau = torch.empty((B, H), dtype=torch.float32, device=grids.device)
+    _dev_tensor(grad_tau, "grad_tau", torch.float32, grids.device)
+    if tuple(grad_tau.shape) != (B, H):
+        raise ValueError("grad_tau must be [B, H]")
+    s = _stream(grids)
+    nb = workspace_bytes_batched(_lib.ECC_OP_SOFT_BWD, B, H)
+    ws = get_workspace(nb, grids.device, s) if ws is None else ws
+    check(lib.ecc_soft_bwd_tau_batched(_ptr(grids), grids.dim() - 1, ctypes.cast(shp, ctypes.c_void_p), B,
+                                       _ptr(tau), ts, H, float(lam), _ptr(grad_out), _ptr(grad_tau), _ptr(ws),
+                                       ws.numel() * ws.element_size(), ctypes.c_void_p(s.cuda_stream)),
+          "ecc_soft_bwd_tau_batched")
+    return grad_tau
+
+
+def ecc_soft_bwd_grid_batched(grids, tau, lam, grad_out, grad_grid=None):
+    """dL/dgrids of a batch, float32 of the grids' shape (see include/ecc.h)."""
+    B, H, ts, shp = _batch_args(grids, tau)
+    _dev_tensor(grad_out, "grad_out", torch.float32, grids.device)
+    if tuple(grad_out.shape) != (B, H):
+        raise ValueError("grad_out must be [B, H]")
+    if grad_grid is None:
+        grad_grid = torch.empty_like(grids)
+    _dev_tensor(grad_grid, "grad_grid", torch.float32, grids.device)
+    if grad_grid.shape != grids.shape:
+        raise ValueError("grad_grid must have the grids' shape")
+    s = _stream(grids)
+    check(lib.ecc_soft_bwd_grid_batched(_ptr(grids), grids.dim() - 1, ctypes.cast(shp, ctypes.c_void_p), B,
+                                        _ptr(tau), ts, H, float(lam), _ptr(grad_out), _ptr(grad_grid),
+                                        ctypes.c_void_p(s.cuda_stream)),
+          "ecc_soft_bwd_grid_batched")
+    return grad_grid
+
+
+class SoftECCBatched(torch.autograd.Function):
+    """Autograd wrapper over a batch: grids [B, ...], tau [H] (shared) or [B, H] -> [B, H]."""
+
+    @staticmethod
+    def forward(ctx, grids, tau, lam):
+        ctx.save_for_backward(grids, tau)
+        ctx.lam = float(lam)
+        return ecc_soft_fwd_batched(grids.detach().contiguous(), tau.detach().contiguous(), lam)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        grids, tau = ctx.saved_tensors
+        grids = grids.detach().contiguous()
+        tau_c = tau.detach().contiguous()
+        grad_out = grad_out.contiguous()
+        g_grid = g_tau = None
+        if ctx.needs_input_grad[0]:
+            g_grid = ecc_soft_bwd_grid_batched(grids, tau_c, ctx.lam, grad_out)
+        if ctx.needs_input_grad[1]:
+            g_tau = ecc_soft_bwd_tau_batched(grids, tau_c, ctx.lam, grad_out)
+            if tau.dim() == 1:
+                g_tau = g_tau.sum(0)  # one threshold array shared by every grid
+        return g_grid, g_tau, None
+
+
+def soft_ecc_batched(grids, tau, lam):
+    """Soft ECC of a batch of grids as an autograd op (differentiable in grids and tau)."""
+    return SoftECCBatched.apply(grids, tau, lam)

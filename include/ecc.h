@@ -170,6 +170,36 @@ int ecc_soft_bwd_grid(const float* grid, int32_t ndim, const int64_t* shape, con
                       int32_t H, float lambda, const float* grad_out, float* grad_grid, void* stream);
 
 /*
+ * Batched soft ECC: `batch` grids of one shape `shape` (HOST array of ndim
+ * entries, the shape of ONE grid), stored back to back.  Grid b uses
+ * tau + b * tau_stride (0: shared thresholds) and, for the backward calls,
+ * grad_out + b * H.  Outputs:
+ *   ecc_soft_fwd_batched       out[b][k]        float32[batch][H]
+ *   ecc_soft_bwd_tau_batched   grad_tau[b][k]   float32[batch][H], the
+ *                              contribution of grid b (with shared thresholds
+ *                              the gradient of tau is the sum over b)
+ *   ecc_soft_bwd_grid_batched  grad_grid        float32[batch][shape...]
+ * Each grid is computed with the arithmetic of the single-grid call; the
+ * split of its cells among workgroups depends on the batch size, so the
+ * curves agree with single calls to float64 rounding of the workgroup sums
+ * (the grid gradient, one value per voxel, agrees bit for bit).  The workspace of the
+ * first two is ecc_workspace_bytes_batched(ECC_OP_SOFT_*, batch, H) bytes,
+ * with the zero-fill convention above; the grid gradient needs none.  One
+ * kernel launch per 65535 grids.  Batches are how the differentiable layer
+ * meets training-scale inputs (section "Limitations and outlook").
+ */
+int ecc_soft_fwd_batched(const float* grid, int32_t ndim, const int64_t* shape, int64_t batch,
+                         const float* tau, int64_t tau_stride, int32_t H, float lambda, float* out, void* ws,
+                         size_t ws_bytes, void* stream);
+int ecc_soft_bwd_tau_batched(const float* grid, int32_t ndim, const int64_t* shape, int64_t batch,
+                             const float* tau, int64_t tau_stride, int32_t H, float lambda,
+                             const float* grad_out, float* grad_tau, void* ws, size_t ws_bytes,
+                             void* stream);
+int ecc_soft_bwd_grid_batched(const float* grid, int32_t ndim, const int64_t* shape, int64_t batch,
+                              const float* tau, int64_t tau_stride, int32_t H, float lambda,
+                              const float* grad_out, float* grad_grid, void* stream);
+
+/*
  * Bytes of workspace needed by an operation (ECC_OP_*) for a grid of `ndim`
  * dimensions `shape` (host array; may be NULL, the size does not depend on
  * it today) and H thresholds.  Returns 0 for invalid op/H.

@@ -28,6 +28,7 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
         "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
         "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
+        "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_grid_batched",
         "ecc_workspace_bytes", "ecc_workspace_bytes_batched", "ecc_status_string", "ecc_last_error",
         "ecc_version"])
 
@@ -172,6 +173,31 @@ def test_soft_grid_argument_errors(L):
         assert soft_grid(L, lam=lam) == L.ECC_E_LAMBDA
     assert soft_grid(L, H=0) == L.ECC_E_NTHRESH
     assert soft_grid(L, H=8193) == L.ECC_E_NTHRESH
+
+
+@pytest.mark.parametrize("which", ["fwd", "bwd_tau", "bwd_grid"])
+def test_soft_batched_argument_errors(L, which):
+    def call(B=2, ts=0, H=4, lam=1.0, ws=FAKE, wsb=1 << 40, gout=FAKE, shape=(4, 4, 4), grid=FAKE):
+        arr = (ctypes.c_int64 * len(shape))(*shape)
+        sp = ctypes.cast(arr, ctypes.c_void_p)
+        if which == "fwd":
+            return L.lib.ecc_soft_fwd_batched(grid, len(shape), sp, B, FAKE, ts, H, lam, FAKE, ws, wsb, None)
+        if which == "bwd_tau":
+            return L.lib.ecc_soft_bwd_tau_batched(grid, len(shape), sp, B, FAKE, ts, H, lam, gout, FAKE, ws, wsb,
+                                                  None)
+        return L.lib.ecc_soft_bwd_grid_batched(grid, len(shape), sp, B, FAKE, ts, H, lam, gout, FAKE, None)
+    assert call(grid=None) == L.ECC_E_NULL
+    assert call(B=0) == L.ECC_E_SHAPE
+    assert call(ts=-4) == L.ECC_E_SHAPE
+    assert call(shape=(3, 0)) == L.ECC_E_SHAPE
+    assert call(B=1 << 30, shape=(1 << 6, 1 << 6, 1 << 6)) == L.ECC_E_SHAPE
+    assert call(lam=0.0) == L.ECC_E_LAMBDA
+    assert call(H=0) == L.ECC_E_NTHRESH
+    if which != "fwd":
+        assert call(gout=None) == L.ECC_E_NULL
+    if which != "bwd_grid":
+        assert call(ws=None) == L.ECC_E_WORKSPACE
+        assert call(wsb=L.lib.ecc_workspace_bytes_batched(1, 2, 4) - 1) == L.ECC_E_WORKSPACE
 
 
 def test_binding_rejects_cpu_tensors():

@@ -1,8 +1,9 @@
-"""GPU parity of the batched hard ECC (B grids per call -> int64[B, H]).
+"""GPU parity of the batched calls (B grids of one shape per call).
 
-Every row must equal the oracle's curve of that grid, bit for bit, for shared
-thresholds ([H]) and per-grid thresholds ([B, H]).  Every case names itself
-before its GPU step.
+Hard: every row of int64[B, H] must equal the oracle's curve of that grid, bit
+for bit, for shared thresholds ([H]) and per-grid thresholds ([B, H]).  Soft:
+every grid's forward, threshold gradient and grid gradient within the soft
+tolerance of the oracle.  Every case names itself before its GPU step.
 """
 
 import zlib
@@ -12,7 +13,7 @@ import pytest
 
 import oracle
 from euler_characteristic_curves_amd import workloads as W
-from tests.gpu_util import banner, need_gpu
+from tests.gpu_util import banner, need_gpu, soft_close
 
 pytestmark = pytest.mark.gpu
 
@@ -133,3 +134,109 @@ def test_batched_workspace_reuse(E):
             torch.cuda.synchronize()
             assert np.array_equal(out.cpu().numpy(), want)
     assert int(torch.count_nonzero(ws).item()) == 0
+
+
+# ------------------------------------------------------------ soft batches
+
+def _soft_batched_gpu(E, g, tau, lam, gout):
+    import torch
+    dg, dt, dgo = _dev(g), _dev(np.asarray(tau, np.float32)), _dev(np.asarray(gout, np.float32))
+    f = E.ecc_soft_fwd_batched(dg, dt, lam)
+    b = E.ecc_soft_bwd_tau_batched(dg, dt, lam, dgo)
+    gg = E.ecc_soft_bwd_grid_batched(dg, dt, lam, dgo)
+    torch.cuda.synchronize()
+    return (f.cpu().numpy().astype(np.float64), b.cpu().numpy().astype(np.float64),
+            gg.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("shape", [(31, 47), (128, 128), (3, 4, 5), (17, 19, 23)])
+@pytest.mark.parametrize("B", [1, 3, 16])
+@pytest.mark.parametrize("per_grid", [False, True])
+def test_soft_batched(E, shape, B, per_grid):
+    rng = np.random.default_rng(zlib.crc32(repr(("soft-b", shape, B, per_grid)).encode()))
+    g = rng.random((B,) + shape, dtype=np.float32)
+    if per_grid:
+        tau = np.stack([W.tau_linspace(-0.1 * b, 1.0 + 0.05 * b, 128) for b in range(B)])
+    else:
+        tau = W.tau_linspace(-0.05, 1.05, 128)
+    gout = rng.standard_normal((B, 128)).astype(np.float32)
+    lam = 40.0
+    banner("soft batched", shape, B, "per-grid" if per_grid else "shared")
+    f, bt, gg = _soft_batched_gpu(E, g, tau, lam, gout)
+    for b in range(B):
+        tb = tau[b] if per_grid else tau
+        bad, worst = soft_close(f[b], oracle.ecc_soft(g[b], tb, lam))
+        assert bad.size == 0, ("fwd", b, worst)
+        bad, worst = soft_close(bt[b], oracle.ecc_soft_bwd_tau(g[b], tb, lam, gout[b]))
+        assert bad.size == 0, ("bwd_tau", b, worst)
+        bad, worst = soft_close(gg[b].ravel(), oracle.ecc_soft_bwd_grid(g[b], tb, lam, gout[b]).ravel())
+        assert bad.size == 0, ("bwd_grid", b, worst)
+
+
+def test_soft_batched_matches_single_calls(E):
+    """The grid gradient of a batch equals single calls bit for bit; the curves
+    agree to float64 rounding of the workgroup sums."""
+    import torch
+    rng = np.random.default_rng(240)
+    g = rng.random((5, 40, 41, 42), dtype=np.float32)
+    tau = W.tau_linspace(0, 1, 256)
+    gout = rng.standard_normal((5, 256)).astype(np.float32)
+    banner("soft batched vs single")
+    f, bt, gg = _soft_batched_gpu(E, g, tau, 50.0, gout)
+    dt = _dev(tau)
+    for b in range(5):
+        dg, dgo = _dev(g[b]), _dev(gout[b])
+        f1 = E.ecc_soft_fwd(dg, dt, 50.0)
+        b1 = E.ecc_soft_bwd_tau(dg, dt, 50.0, dgo)
+        g1 = E.ecc_soft_bwd_grid(dg, dt, 50.0, dgo)
+        torch.cuda.synchronize()
+        assert np.array_equal(gg[b], g1.cpu().numpy().astype(np.float64))
+        assert np.max(np.abs(f[b] - f1.cpu().numpy())) <= 1e-6 * max(1.0, np.max(np.abs(f[b])))
+        assert np.max(np.abs(bt[b] - b1.cpu().numpy())) <= 1e-6 * max(1.0, np.max(np.abs(bt[b])))
+
+
+def test_soft_batched_more_than_one_launch(E):
+    """70000 tiny grids (two launches); 8 distinct grids repeat through the batch."""
+    rng = np.random.default_rng(250)
+    proto = rng.random((8, 2, 3), dtype=np.float32)
+    B = 70000
+    g = proto[np.arange(B) % 8]
+    tau = W.tau_linspace(0, 1, 16)
+    gout = np.tile(rng.standard_normal((8, 16)).astype(np.float32), (B // 8, 1))
+    banner("soft batched 70000 2x3")
+    f, bt, gg = _soft_batched_gpu(E, g, tau, 20.0, gout)
+    for p in range(8):
+        rows = np.arange(p, B, 8)
+        bad, worst = soft_close(f[rows].ravel(), np.tile(oracle.ecc_soft(proto[p], tau, 20.0), rows.size))
+        assert bad.size == 0, worst
+        want_b = oracle.ecc_soft_bwd_tau(proto[p], tau, 20.0, gout[p])
+        bad, worst = soft_close(bt[rows].ravel(), np.tile(want_b, rows.size))
+        assert bad.size == 0, worst
+        want_g = oracle.ecc_soft_bwd_grid(proto[p], tau, 20.0, gout[p]).ravel()
+        bad, worst = soft_close(gg[rows].reshape(rows.size, -1).ravel(), np.tile(want_g, rows.size))
+        assert bad.size == 0, worst
+
+
+def test_soft_batched_autograd(E):
+    import torch
+    rng = np.random.default_rng(260)
+    B = 4
+    g = _dev(rng.random((B, 18, 19, 20), dtype=np.float32)).requires_grad_(True)
+    tau = torch.tensor(W.tau_linspace(0, 1, 48)).cuda().requires_grad_(True)
+    w = rng.standard_normal((B, 48)).astype(np.float32)
+    banner("soft batched autograd")
+    s = E.soft_ecc_batched(g, tau, 30.0)
+    assert tuple(s.shape) == (B, 48)
+    (s * torch.from_numpy(w).cuda()).sum().backward()
+    gn, tn = g.detach().cpu().numpy(), tau.detach().cpu().numpy()
+    want_tau = sum(oracle.ecc_soft_bwd_tau(gn[b], tn, 30.0, w[b]) for b in range(B))
+    bad, worst = soft_close(tau.grad.cpu().numpy(), want_tau)
+    assert bad.size == 0, worst
+    for b in range(B):
+        bad, worst = soft_close(g.grad[b].cpu().numpy().ravel(),
+                                oracle.ecc_soft_bwd_grid(gn[b], tn, 30.0, w[b]).ravel())
+        assert bad.size == 0, (b, worst)
+    # per-grid thresholds: their gradient keeps the batch dimension
+    tau2 = torch.tensor(np.stack([W.tau_linspace(0, 1, 48)] * B)).cuda().requires_grad_(True)
+    E.soft_ecc_batched(g.detach(), tau2, 30.0).sum().backward()
+    assert tuple(tau2.grad.shape) == (B, 48)
