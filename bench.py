@@ -106,21 +106,23 @@ def recorded_traffic():
         return None
 
 
-def recorded_soft_valu():
-    """(forward, tau-backward, grid-backward) VALU wave-instructions per soft
-    launch at 256^3, H=256.
+def recorded_soft_valu(kind="issue"):
+    """(forward, tau-backward, grid-backward) VALU work per soft launch at
+    256^3, H=256, from the committed rocprofv3 SQ profile.
 
-    The counts are fixed by the kernels and their input; they come from the
-    committed rocprofv3 SQ_INSTS_VALU profile and are used only while the soft
-    sources hash to the value recorded there.
+    kind="issue": SQ_ACTIVE_INST_VALU, the VALU issue slots the waves occupy
+    (a transcendental takes two); kind="instr": SQ_INSTS_VALU, instructions.
+    Both are fixed by the kernels and their input, and are used only while the
+    soft sources hash to the value recorded in the profile.
     """
     fields = profile_fields(SQ_PROFILE)
     if fields.get("soft_source_sha256") != source_hash(SOFT_SOURCES):
         return None, None, None
+    suffix = "valu_issue_slots" if kind == "issue" else "valu_wave_instr"
     out = []
-    for key in ("soft_fwd_valu_wave_instr", "soft_bwd_valu_wave_instr", "soft_grad_valu_wave_instr"):
+    for op in ("fwd", "bwd", "grad"):
         try:
-            out.append(float(fields[key]))
+            out.append(float(fields[f"soft_{op}_{suffix}"]))
         except (KeyError, ValueError):
             out.append(None)
     return tuple(out)
@@ -389,7 +391,8 @@ def main():
         torch.cuda.synchronize()
         grad_nonzero = int(torch.count_nonzero(dgg).item())
         pairs = n_cells(gs.shape) * ts.size
-        vf, vb, vg = recorded_soft_valu()
+        vf, vb, vg = recorded_soft_valu("issue")
+        nf, nb, ng = recorded_soft_valu("instr")
 
         def frac(v, ms):
             return None if v is None else v / (ms * 1e-3) / VALU_WAVE_INSTR_PEAK
@@ -403,9 +406,11 @@ def main():
             "bwd_grid_voxels_per_s": gs.size / (msg * 1e-3),
             "bwd_grid_nonzero_voxels": grad_nonzero,
             "bwd_grid_voxel_threshold_pairs_per_s": grad_nonzero * ts.size / (msg * 1e-3),
-            "roofline": {"bound": "valu", "unit": "wave64 VALU instr/s", "peak": VALU_WAVE_INSTR_PEAK,
+            "roofline": {"bound": "valu", "unit": "wave64 VALU issue slots/s", "peak": VALU_WAVE_INSTR_PEAK,
                          "fwd_frac": frac(vf, msf), "bwd_frac": frac(vb, msb), "bwd_grid_frac": frac(vg, msg),
-                         "valu_instr_per_launch": {"fwd": vf, "bwd": vb, "bwd_grid": vg}},
+                         "valu_issue_slots_per_launch": {"fwd": vf, "bwd": vb, "bwd_grid": vg},
+                         "valu_instr_per_launch": {"fwd": nf, "bwd": nb, "bwd_grid": ng},
+                         "instr_frac": {"fwd": frac(nf, msf), "bwd": frac(nb, msb), "bwd_grid": frac(ng, msg)}},
         }
 
     vox_step = n3 + n4

@@ -14,8 +14,11 @@
 // exact regrouping as the hard kernels (four row sequences per voxel,
 // telescoped along x, equal values merged), so a term carries the summed sign
 // of every cell that has that value.  Phase B sweeps the list in LDS against
-// the thresholds: every lane owns 4 thresholds per 256-threshold chunk and
-// every wave a quarter of the terms.  The sigmoid costs one FMA and one
+// the thresholds: every wave takes a quarter of the terms, four at a time
+// (one per 16-lane group), and every lane owns 16 thresholds of each
+// 256-threshold chunk, so one broadcast LDS read of a term feeds 16 sigmoids
+// per lane and the sweep's LDS traffic stays well below its VALU work.  The
+// sigmoid costs one FMA and one
 // reciprocal per (term, threshold) in the factored form
 //     exp(lambda (v - tau)) = 2^{L (v - c)} * 2^{L (c - tau)},  L = lambda log2 e,
 // with the first factor computed once per term and the second once per
@@ -35,7 +38,10 @@ namespace {
 
 constexpr int kTileVox = 1024;          // voxels per tile
 constexpr int kTermCap = 4 * kTileVox;  // at most 4 terms per voxel
-constexpr int kChunk = 256;             // thresholds per sweep chunk (4 per lane)
+constexpr int kChunk = 256;             // thresholds per sweep chunk
+constexpr int kLaneGroups = 4;          // terms a wave sweeps at once
+constexpr int kGroupLanes = 64 / kLaneGroups;
+constexpr int kSlots = kChunk / kGroupLanes;  // thresholds per lane and chunk
 
 struct Term {
   float a;  // F = 2^{L (v - c)} (factored) or the value v (direct)
@@ -175,26 +181,39 @@ __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles
     const int n = misc[0];
 
     // ---------------- phase B: sweep terms x thresholds
+    // A wave works on kLaneGroups terms at once, one per group of
+    // kGroupLanes lanes; a lane owns kSlots thresholds of the chunk, so each
+    // broadcast read of a term serves kSlots sigmoids per lane.
     const int tb = (int)(((int64_t)n * wave) / kWavesPerBlock);
     const int te = (int)(((int64_t)n * (wave + 1)) / kWavesPerBlock);
+    const int grp = lane / kGroupLanes, gl = lane % kGroupLanes;
     for (int c = 0; c < nchunks; ++c) {
-      float e[4];
-      bool valid[4];
+      float e[kSlots];
+      bool valid[kSlots];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int k = c * kChunk + r * 64 + lane;
+      for (int r = 0; r < kSlots; ++r) {
+        const int k = c * kChunk + r * kGroupLanes + gl;
         valid[r] = k < H;
         const float tk = valid[r] ? p.tau[k] : 0.0f;
         e[r] = factored ? (valid[r] ? exp2_split(L64 * (cen - (double)tk)) : 0.0f) : tk;
       }
-      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+      double acc[kSlots];
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r) acc[r] = 0.0;
+      // groups past the wave's last term take its first one with weight 0
+      auto term = [&](int base) {
+        const int ti = base + grp;
+        Term tm = terms[ti < te ? ti : tb];
+        if (ti >= te) tm.w = 0.0f;
+        return tm;
+      };
       if (factored) {
-        for (int ti = tb; ti < te; ++ti) {
-          const Term tm = terms[ti];
+        for (int base = tb; base < te; base += kLaneGroups) {
+          const Term tm = term(base);
           const double wd = (double)tm.w;
           const float wf = tm.w * tm.a;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
+          for (int r = 0; r < kSlots; ++r) {
             const float d = fmaf(tm.a, e[r], 1.0f);
             const float rr = __builtin_amdgcn_rcpf(d);
             if constexpr (!BWD) {
@@ -206,11 +225,11 @@ __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles
           }
         }
       } else {
-        for (int ti = tb; ti < te; ++ti) {
-          const Term tm = terms[ti];
+        for (int base = tb; base < te; base += kLaneGroups) {
+          const Term tm = term(base);
           const double wd = (double)tm.w;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
+          for (int r = 0; r < kSlots; ++r) {
             const float x = fminf(Lf * (tm.a - e[r]), 126.0f);  // L (v - tau), kept finite
             const float tt = __builtin_amdgcn_exp2f(x);
             const float rr = __builtin_amdgcn_rcpf(1.0f + tt);
@@ -224,8 +243,8 @@ __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (valid[r]) atomicAdd(&accS[c * kChunk + r * 64 + lane], acc[r]);
+      for (int r = 0; r < kSlots; ++r)
+        if (valid[r]) atomicAdd(&accS[c * kChunk + r * kGroupLanes + gl], acc[r]);
     }
     __syncthreads();
     if (tid == 0) misc[0] = 0;
