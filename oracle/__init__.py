@@ -29,6 +29,11 @@ Pinning status (what checks this oracle against something other than itself):
                                each voxel on tie-free grids, the sum rule
                                (translating the grid by s moves every cell
                                value by s), per-voxel vs scatter agreement.
+  * height_values / height_bwd -- pinned: hand-computed heights, the
+                               directional curve of a box (a step) and of a
+                               frame (0, 1, 0) by brute force, central finite
+                               differences of the whole soft pipeline in u,
+                               alpha and the grid.
   * at the 256^3 soft size the only check is the per-cell vs grouped
     agreement of this same oracle: parity unpinned beyond that.
 """
@@ -39,6 +44,8 @@ from .ecc import (  # noqa: F401
     first_k_bins,
     ecc_hard,
     ecc_hard_batched,
+    height_values,
+    height_bwd,
     ecc_at,
     ecc_at_many,
     ecc_soft,

@@ -28,6 +28,7 @@ __all__ = [
     "sigmoid", "ecc_soft", "ecc_soft_percell", "ecc_soft_at",
     "ecc_soft_bwd_tau", "ecc_soft_bwd_at", "ecc_at_many", "ecc_soft_at_many",
     "ecc_soft_bwd_at_many", "ecc_soft_bwd_grid", "ecc_soft_bwd_grid_at", "ecc_hard_batched",
+    "height_values", "height_bwd",
 ]
 
 
@@ -419,3 +420,58 @@ def ecc_hard_batched(grids, tau):
         raise ValueError("grids must be [B, ny, nx] or [B, nz, ny, nx]")
     rows = [ecc_hard(grids[b], tau if tau.ndim == 1 else tau[b]) for b in range(grids.shape[0])]
     return np.stack(rows)
+
+
+# ------------------------------------------------------- directional heights
+# The page's single-direction layer adds a learnable direction u and scale
+# alpha, with gradients through both, and names the multi-direction transform
+# as the complete version (sections "Method / Key designs / differentiable ECC
+# layer" and "Limitations and outlook").  It does not define the height
+# function on a grid; the reading taken here is
+#     f_d(p) = X(p) + alpha_d * <u_d, p>,
+# with p the integer voxel index (slowest axis first).  A voxel at +inf never
+# enters, so X = 0 on a shape and +inf off it gives the shape's directional
+# filtration, and a plain intensity grid gets a tilted one.  The curves of
+# direction d are those of the grid f_d.
+
+def height_values(grid, dirs, alpha):
+    """f[d] = grid + alpha[d] * <dirs[d], p> in float32, float32[D, *shape].
+
+    The arithmetic is fixed so that it can be reproduced bit for bit: each
+    product and sum rounded to float32 in the order
+        h = (u_0 p_0 + u_1 p_1) [+ u_2 p_2],   f = X + alpha * h,
+    with no fused multiply-add.
+    """
+    X = np.asarray(grid, dtype=np.float32)
+    if X.ndim not in (2, 3):
+        raise ValueError("grid must be 2D or 3D")
+    U = np.asarray(dirs, dtype=np.float32).reshape(-1, X.ndim)
+    A = np.asarray(alpha, dtype=np.float32).reshape(-1)
+    if A.size != U.shape[0]:
+        raise ValueError("one alpha per direction")
+    idx = [np.arange(n, dtype=np.float32).reshape([-1 if a == i else 1 for a in range(X.ndim)])
+           for i, n in enumerate(X.shape)]
+    out = np.empty((U.shape[0],) + X.shape, dtype=np.float32)
+    for d in range(U.shape[0]):
+        h = np.float32(U[d, 0]) * idx[0]
+        for i in range(1, X.ndim):
+            h = h + np.float32(U[d, i]) * idx[i]
+        out[d] = X + np.float32(A[d]) * h
+    return out
+
+
+def height_bwd(grad_h, dirs, alpha):
+    """Chain rule of height_values, float64.
+
+    Given G[d] = dL/df[d]: dL/dX = sum_d G[d]; with M[d, i] = sum_p G[d](p) p_i,
+    dL/du[d, i] = alpha[d] M[d, i] and dL/dalpha[d] = sum_i u[d, i] M[d, i].
+    """
+    G = np.asarray(grad_h, dtype=np.float64)
+    nd = G.ndim - 1
+    U = np.asarray(dirs, dtype=np.float32).astype(np.float64).reshape(-1, nd)
+    A = np.asarray(alpha, dtype=np.float32).astype(np.float64).reshape(-1)
+    M = np.zeros((G.shape[0], nd))
+    for i, n in enumerate(G.shape[1:]):
+        coord = np.arange(n, dtype=np.float64).reshape([-1 if a == i else 1 for a in range(nd)])
+        M[:, i] = (G * coord).reshape(G.shape[0], -1).sum(axis=1)
+    return G.sum(axis=0), A[:, None] * M, (U * M).sum(axis=1)

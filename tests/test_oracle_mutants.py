@@ -204,3 +204,34 @@ def test_unpatched_grid_gradient_passes_pins():
 def test_grid_gradient_mutants_are_caught(monkeypatch, kind):
     monkeypatch.setattr(oracle, "ecc_soft_bwd_grid", _grad_mutant(kind))
     assert not _run_grad_pins()
+
+
+# ------------------------------------------------- directional height mutants
+def test_height_axis_order_mutant_is_caught(monkeypatch):
+    """Heights with the axes taken fastest first fail the hand-worked values."""
+    real = oecc.height_values
+
+    def reversed_axes(grid, dirs, alpha):
+        X = np.asarray(grid, np.float32)
+        U = np.asarray(dirs, np.float32).reshape(-1, X.ndim)[:, ::-1]
+        return real(X, U, alpha)
+
+    monkeypatch.setattr(oracle, "height_values", reversed_axes)
+    from tests import test_oracle_pins as P
+    with pytest.raises(AssertionError):
+        P.test_height_values_by_hand()
+
+
+def test_height_bwd_without_alpha_is_caught(monkeypatch):
+    """A backward that forgets alpha in dL/du fails the finite differences."""
+    real = oecc.height_bwd
+
+    def no_alpha(grad_h, dirs, alpha):
+        dX, dU, dA = real(grad_h, dirs, alpha)
+        a = np.asarray(alpha, np.float32).astype(np.float64).reshape(-1, 1)
+        return dX, dU / a, dA
+
+    monkeypatch.setattr(oracle, "height_bwd", no_alpha)
+    from tests import test_oracle_pins as P
+    with pytest.raises(AssertionError):
+        P.test_height_gradient_finite_differences((4, 5))

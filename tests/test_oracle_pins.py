@@ -420,3 +420,88 @@ def test_batched_oracle_is_per_grid():
     # all grids at their max: each contributes 1, while the 3D stack is one box (also 1),
     # but below the max the 3D stack joins grids through z-edges
     assert not np.array_equal(oracle.ecc_hard_batched(g, tau).sum(0), oracle.ecc_hard(g, tau))
+
+
+# ------------------------------------------------------ directional heights
+def test_height_values_by_hand():
+    """f = X + alpha * <u, p>, p the integer index, slowest axis first."""
+    X = np.array([[0.0, 1.0, 0.0], [2.0, 0.0, np.inf]], np.float32)
+    f = oracle.height_values(X, [[1.0, 2.0], [-1.0, 0.5]], [0.5, 2.0])
+    np.testing.assert_array_equal(f[0], [[0.0, 2.0, 2.0], [2.5, 1.5, np.inf]])
+    np.testing.assert_array_equal(f[1], [[0.0, 2.0, 2.0], [0.0, -1.0, np.inf]])
+    X3 = np.zeros((2, 2, 2), np.float32)
+    f3 = oracle.height_values(X3, [0.25, -2.0, 4.0], [1.0])[0]
+    for z, y, x in np.ndindex(2, 2, 2):
+        assert f3[z, y, x] == 0.25 * z - 2.0 * y + 4.0 * x
+
+
+@pytest.mark.parametrize("shape", [(6, 9), (4, 5, 7)])
+def test_directional_curve_of_a_box_is_a_step(shape):
+    """Every sublevel set of a linear height on the full box is a staircase,
+    contractible when not empty: the curve is 0 below the minimum, 1 above."""
+    rng = np.random.default_rng(98)
+    X = np.zeros(shape, np.float32)
+    for _ in range(4):
+        u = rng.normal(size=len(shape)).astype(np.float32)
+        f = oracle.height_values(X, u, [0.75])[0]
+        tau = np.linspace(float(f.min()) - 1, float(f.max()) + 1, 41).astype(np.float32)
+        want = (tau >= f.min()).astype(np.int64)
+        assert oracle.ecc_hard(f, tau).tolist() == want.tolist()
+
+
+def test_directional_curve_of_a_frame():
+    """A 7x9 frame around a 3x5 hole swept along x: a solid block, then a C,
+    then the closed ring once its right column enters (0, 1, ..., 1, 0)."""
+    X = np.zeros((7, 9), np.float32)
+    X[2:5, 2:7] = np.inf
+    f = oracle.height_values(X, [0.0, 1.0], [1.0])[0]
+    tau = np.arange(-1, 10, dtype=np.float32)
+    want = [0] + [1] * 7 + [0] * 3
+    assert [pins.brute_chi(f, float(t)) for t in tau] == want
+    assert oracle.ecc_hard(f, tau).tolist() == want
+
+
+@pytest.mark.parametrize("shape", [(4, 5), (2, 3, 4)])
+def test_height_gradient_finite_differences(shape):
+    """dL/du, dL/dalpha and dL/dX of L = sum_d sum_k g[d,k] S_k(f_d) against
+    central differences of the whole pipeline, each f_d formed in float64 here
+    and its soft curve summed cell by cell (tests/pins.py)."""
+    rng = np.random.default_rng(99)
+    nd = len(shape)
+    n = int(np.prod(shape))
+    X = (rng.permutation(n) / n).reshape(shape)           # tie-free
+    U = np.array([[0.8125, -0.4375, 0.3125][:nd], [-0.25, 0.6875, 0.5625][:nd]], np.float32)
+    A = np.array([0.1875, -0.125], np.float32)
+    lam = 7.0
+    tau = np.linspace(-0.5, 1.5, 9).astype(np.float32)
+    g = rng.standard_normal((2, tau.size)).astype(np.float32)
+    coords = np.indices(shape).astype(np.float64)
+
+    def heights(X, U, A):
+        return [X + float(A[d]) * sum(float(U[d, i]) * coords[i] for i in range(nd)) for d in range(2)]
+
+    def loss(X, U, A):
+        return sum(float(np.dot(g[d].astype(np.float64), pins.soft_by_hand(f, tau, lam)))
+                   for d, f in enumerate(heights(X, U, A)))
+
+    G = np.stack([oracle.ecc_soft_bwd_grid(f, tau, lam, g[d]) for d, f in enumerate(heights(X, U, A))])
+    dX, dU, dA = oracle.height_bwd(G, U, A)
+    h = 1e-6
+    for d in range(2):
+        for i in range(nd):
+            up, dn = U.astype(np.float64).copy(), U.astype(np.float64).copy()
+            up[d, i] += h
+            dn[d, i] -= h
+            fd = (loss(X, up, A) - loss(X, dn, A)) / (2 * h)
+            assert abs(fd - dU[d, i]) < 1e-5 * max(1.0, abs(fd)), ("u", d, i, fd, dU[d, i])
+        up, dn = A.astype(np.float64).copy(), A.astype(np.float64).copy()
+        up[d] += h
+        dn[d] -= h
+        fd = (loss(X, U, up) - loss(X, U, dn)) / (2 * h)
+        assert abs(fd - dA[d]) < 1e-5 * max(1.0, abs(fd)), ("alpha", d, fd, dA[d])
+    for p in list(np.ndindex(*shape))[::3]:
+        up, dn = X.copy(), X.copy()
+        up[p] += h
+        dn[p] -= h
+        fd = (loss(up, U, A) - loss(dn, U, A)) / (2 * h)
+        assert abs(fd - dX[p]) < 1e-5 * max(1.0, abs(fd)), ("X", p, fd, dX[p])
