@@ -18,17 +18,20 @@ ECC_E_NTHRESH = 4
 ECC_E_LAMBDA = 5
 ECC_E_WORKSPACE = 6
 ECC_E_HIP = 7
+ECC_E_NDIRS = 8
 ECC_U8 = 0
 ECC_F32 = 1
 ECC_OP_HARD = 0
 ECC_OP_SOFT_FWD = 1
 ECC_OP_SOFT_BWD = 2
 ECC_MAX_THRESHOLDS = 8192
+ECC_MAX_DIRECTIONS = 4096
 
 EXPORTS = (
     "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
     "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
     "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_grid_batched",
+    "ecc_height", "ecc_height_bwd", "ecc_height_workspace_bytes",
     "ecc_workspace_bytes", "ecc_workspace_bytes_batched", "ecc_status_string", "ecc_last_error", "ecc_version",
 )
 
@@ -69,6 +72,12 @@ def _load():
     lib.ecc_soft_bwd_tau_batched.restype = I
     lib.ecc_soft_bwd_grid_batched.argtypes = [P, I32, P, I64, P, I64, I32, F, P, P, P]
     lib.ecc_soft_bwd_grid_batched.restype = I
+    lib.ecc_height.argtypes = [P, I32, P, P, P, I32, P, P]
+    lib.ecc_height.restype = I
+    lib.ecc_height_bwd.argtypes = [P, I32, P, P, P, I32, P, P, P, P, SZ, P]
+    lib.ecc_height_bwd.restype = I
+    lib.ecc_height_workspace_bytes.argtypes = [I32, I32]
+    lib.ecc_height_workspace_bytes.restype = SZ
     lib.ecc_workspace_bytes.argtypes = [I, I32, P, I32]
     lib.ecc_workspace_bytes.restype = SZ
     lib.ecc_workspace_bytes_batched.argtypes = [I, I64, I32]

@@ -99,6 +99,29 @@ int check_soft(const float* grid, int32_t ndim, const int64_t* shape, const floa
   return ECC_OK;
 }
 
+// Checks of the height entry points; fills dims (nz = 1 in 2D).
+int check_height(const void* grid, int32_t ndim, const int64_t* shape, const float* dirs, const float* alpha,
+                 int32_t D, const void* out, int64_t dims[3]) {
+  g_err[0] = 0;
+  if (!grid) return fail(ECC_E_NULL, "%sgrid is NULL");
+  if (!shape) return fail(ECC_E_NULL, "%sshape is NULL");
+  if (!dirs) return fail(ECC_E_NULL, "%sdirs is NULL");
+  if (!alpha) return fail(ECC_E_NULL, "%salpha is NULL");
+  if (!out) return fail(ECC_E_NULL, "%soutput is NULL");
+  if (ndim != 2 && ndim != 3) return fail(ECC_E_SHAPE, "%sndim=%lld, must be 2 or 3", nullptr, ndim);
+  dims[0] = ndim == 3 ? shape[0] : 1;
+  dims[1] = shape[ndim - 2];
+  dims[2] = shape[ndim - 1];
+  for (int i = 0; i < 3; ++i)
+    if (dims[i] < 1 || dims[i] > ECC_MAX_AXIS)
+      return fail(ECC_E_SHAPE, "%severy dimension must be in [1, 2^24]");
+  if (D < 1 || D > ECC_MAX_DIRECTIONS)
+    return fail(ECC_E_NDIRS, "%sD=%lld outside [1, %lld]", nullptr, D, ECC_MAX_DIRECTIONS);
+  const int64_t nvox = dims[0] * dims[1] * dims[2];
+  if (nvox > ECC_MAX_VOXELS / D) return fail(ECC_E_SHAPE, "%sD x voxels exceeds 2^40");
+  return ECC_OK;
+}
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return ECC_OK;
   return fail(ECC_E_HIP, "HIP error: %s", hipGetErrorString(e));
@@ -243,6 +266,60 @@ int ecc_soft_bwd_grid_batched(const float* grid, int32_t ndim, const int64_t* sh
   return hip_status(ecc::launch_soft_grad(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int ecc_height(const float* grid, int32_t ndim, const int64_t* shape, const float* dirs, const float* alpha,
+               int32_t D, float* out, void* stream) {
+  int64_t d[3];
+  int st = check_height(grid, ndim, shape, dirs, alpha, D, out, d);
+  if (st != ECC_OK) return st;
+  ecc::HeightArgs a{};
+  a.grid = grid;
+  a.nd = ndim;
+  a.nz = d[0];
+  a.ny = d[1];
+  a.nx = d[2];
+  a.dirs = dirs;
+  a.alpha = alpha;
+  a.D = D;
+  a.out = out;
+  return hip_status(ecc::launch_height(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int ecc_height_bwd(const float* grad_h, int32_t ndim, const int64_t* shape, const float* dirs, const float* alpha,
+                   int32_t D, float* grad_grid, float* grad_dirs, float* grad_alpha, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int64_t d[3];
+  int st = check_height(grad_h, ndim, shape, dirs, alpha, D, grad_grid ? (void*)grad_grid : (void*)grad_dirs, d);
+  if (st != ECC_OK) return st;
+  if ((grad_dirs == nullptr) != (grad_alpha == nullptr))
+    return fail(ECC_E_NULL, "%sgrad_dirs and grad_alpha must both be given or both be NULL");
+  if (grad_dirs) {
+    if (!ws) return fail(ECC_E_WORKSPACE, "%sworkspace is NULL");
+    const size_t need = ecc::height_workspace_bytes(ndim, D);
+    if (ws_bytes < need)
+      return fail(ECC_E_WORKSPACE, "%sworkspace has %lld bytes, needs %lld", nullptr, (long long)ws_bytes,
+                  (long long)need);
+  }
+  ecc::HeightArgs a{};
+  a.nd = ndim;
+  a.nz = d[0];
+  a.ny = d[1];
+  a.nx = d[2];
+  a.dirs = dirs;
+  a.alpha = alpha;
+  a.D = D;
+  a.grad_h = grad_h;
+  a.grad_grid = grad_grid;
+  a.grad_dirs = grad_dirs;
+  a.grad_alpha = grad_alpha;
+  a.ws = ws;
+  return hip_status(ecc::launch_height_bwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t ecc_height_workspace_bytes(int32_t ndim, int32_t D) {
+  if ((ndim != 2 && ndim != 3) || D < 1 || D > ECC_MAX_DIRECTIONS) return 0;
+  return ecc::height_workspace_bytes(ndim, D);
+}
+
 size_t ecc_workspace_bytes(int op, int32_t ndim, const int64_t* shape, int32_t H) {
   (void)ndim;
   (void)shape;
@@ -267,6 +344,7 @@ const char* ecc_status_string(int status) {
     case ECC_E_LAMBDA: return "lambda must be finite and > 0";
     case ECC_E_WORKSPACE: return "workspace missing or too small";
     case ECC_E_HIP: return "HIP runtime error";
+    case ECC_E_NDIRS: return "number of directions out of range";
     default: return "unknown status";
   }
 }

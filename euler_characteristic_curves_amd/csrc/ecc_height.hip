@@ -1,0 +1,244 @@
+// Directional heights for the single- and multi-direction curves, gfx950.
+//
+// The page's differentiable layer adds a learnable direction u and scale
+// alpha for its single-direction version, and names the multi-direction
+// transform as the complete one (page "Scalable GPU-Accelerated Euler
+// Characteristic Curves", "Method / Key designs / differentiable ECC layer",
+// "Limitations and outlook").  The height of voxel p along direction d is
+//     f_d(p) = X(p) + alpha_d * <u_d, p>,   p = integer voxel index,
+// evaluated in float32 with every product and sum rounded in the order
+//     h = (u_0 p_0 + u_1 p_1) [+ u_2 p_2],   f = X + alpha * h
+// and nothing fused, so the values (and hence the hard curves of f) are
+// reproducible bit for bit.  The curves of direction d are those of the grid
+// f_d, computed by the batched entry points over the D height grids.
+//
+// Backward: with G_d = dL/df_d (the grid gradient of each height grid),
+//     dL/dX = sum_d G_d,
+//     M_d,i = sum_p G_d(p) p_i,  dL/du_d,i = alpha_d M_d,i,  dL/dalpha_d = sum_i u_d,i M_d,i.
+// The moments are float64 per thread and workgroup; each workgroup adds its
+// partial into its own zeroed workspace slot (one device-scope add, so the
+// slot holds the partial exactly) and the last workgroup of the direction
+// sums the slots in order: the result does not depend on scheduling.
+
+#include <hip/hip_runtime.h>
+
+#include "ecc_device.hpp"
+#include "ecc_internal.hpp"
+
+namespace ecc {
+namespace {
+
+constexpr int kHNT = 256;
+constexpr int kHTileX = 4 * kHNT;  // columns per tile: 4 coalesced passes of the workgroup
+
+// Tiles are (row, column block); rows are (z, y) in 3D and y in 2D.
+struct HeightGeom {
+  int64_t n1, nx, nrows, ntx, ntiles, nvox;
+};
+
+__host__ __device__ inline HeightGeom height_geom(const HeightArgs& a) {
+  HeightGeom g;
+  g.n1 = a.ny;
+  g.nx = a.nx;
+  g.nrows = a.nz * a.ny;
+  g.ntx = (a.nx + kHTileX - 1) / kHTileX;
+  g.ntiles = g.nrows * g.ntx;
+  g.nvox = g.nrows * a.nx;
+  return g;
+}
+
+// Height of one voxel, rounded step by step (no contraction into FMAs).
+template <int ND>
+__device__ __forceinline__ float height_of(float X, float alpha, const float* u, float pz, float py, float px) {
+#pragma clang fp contract(off)
+  float h;
+  if constexpr (ND == 3) {
+    const float a = u[0] * pz;
+    const float b = u[1] * py;
+    const float ab = a + b;
+    const float c = u[2] * px;
+    h = ab + c;
+  } else {
+    const float a = u[0] * py;
+    const float c = u[1] * px;
+    h = a + c;
+  }
+  const float s = alpha * h;
+  return X + s;
+}
+
+template <int ND>
+__global__ __launch_bounds__(kHNT) void height_kernel(HeightArgs a) {
+  extern __shared__ float sd[];  // u[D][ND] then alpha[D]
+  const int D = a.D;
+  for (int i = threadIdx.x; i < D * (ND + 1); i += kHNT) sd[i] = i < D * ND ? a.dirs[i] : a.alpha[i - D * ND];
+  __syncthreads();
+  const HeightGeom g = height_geom(a);
+  for (int64_t t = blockIdx.x; t < g.ntiles; t += gridDim.x) {
+    const int64_t row = t / g.ntx, xc = t - row * g.ntx;
+    const int64_t z = ND == 3 ? row / g.n1 : 0, y = row - z * g.n1;
+    float X[4];
+    int64_t xs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xs[j] = xc * kHTileX + j * kHNT + threadIdx.x;
+      X[j] = xs[j] < g.nx ? a.grid[row * g.nx + xs[j]] : 0.0f;
+    }
+    for (int d = 0; d < D; ++d) {
+      const float* u = sd + d * ND;
+      const float al = sd[D * ND + d];
+      float* out = a.out + (size_t)d * (size_t)g.nvox + row * g.nx;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (xs[j] < g.nx) out[xs[j]] = height_of<ND>(X[j], al, u, (float)z, (float)y, (float)xs[j]);
+    }
+  }
+}
+
+// dL/dX = sum over directions, float32 in increasing d.
+__global__ __launch_bounds__(kHNT) void height_grid_grad_kernel(HeightArgs a, int64_t nvox) {
+  const int64_t stride = (int64_t)gridDim.x * kHNT;
+  for (int64_t i = (int64_t)blockIdx.x * kHNT + threadIdx.x; i < nvox; i += stride) {
+    float s = 0.0f;
+    for (int d = 0; d < a.D; ++d) s += a.grad_h[(size_t)d * (size_t)nvox + i];
+    a.grad_grid[i] = s;
+  }
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Moments of direction blockIdx.y, then dL/du and dL/dalpha by its last workgroup.
+template <int ND>
+__global__ __launch_bounds__(kHNT) void height_moments_kernel(HeightArgs a) {
+  __shared__ double red[kHNT / 64][ND];
+  __shared__ double Ms[ND];
+  __shared__ int last;
+  const int d = blockIdx.y;
+  const HeightGeom g = height_geom(a);
+  const float* G = a.grad_h + (size_t)d * (size_t)g.nvox;
+  double m[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) m[i] = 0.0;
+  for (int64_t t = blockIdx.x; t < g.ntiles; t += gridDim.x) {
+    const int64_t row = t / g.ntx, xc = t - row * g.ntx;
+    const int64_t z = ND == 3 ? row / g.n1 : 0, y = row - z * g.n1;
+    double sx = 0.0, s = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t x = xc * kHTileX + j * kHNT + threadIdx.x;
+      if (x < g.nx) {
+        const double v = (double)G[row * g.nx + x];
+        s += v;
+        sx = fma(v, (double)x, sx);
+      }
+    }
+    // the row's voxels share z and y
+    if constexpr (ND == 3) {
+      m[0] = fma(s, (double)z, m[0]);
+      m[1] = fma(s, (double)y, m[1]);
+      m[2] += sx;
+    } else {
+      m[0] = fma(s, (double)y, m[0]);
+      m[1] += sx;
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    const double v = wave_sum(m[i]);
+    if (lane == 0) red[wave][i] = v;
+  }
+  __syncthreads();
+  double* part = reinterpret_cast<double*>(reinterpret_cast<char*>(a.ws) + height_ws_header(a.D)) +
+                 ((size_t)d * gridDim.x + blockIdx.x) * ND;
+  unsigned int* ticket = reinterpret_cast<unsigned int*>(a.ws) + d;
+  if (threadIdx.x < ND) {
+    double v = 0.0;
+    for (int w = 0; w < kHNT / 64; ++w) v += red[w][threadIdx.x];
+    // the slot is zero: this device-scope add leaves exactly v in it
+    __hip_atomic_fetch_add(part + threadIdx.x, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's add is acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned int prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = (prev == gridDim.x - 1);
+    if (last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  double* slots = part - (size_t)blockIdx.x * ND;  // direction d's first slot
+  if (threadIdx.x < ND) {
+    double s = 0.0;
+    for (unsigned int w = 0; w < gridDim.x; ++w) s += agent_load(slots + (size_t)w * ND + threadIdx.x);
+    for (unsigned int w = 0; w < gridDim.x; ++w) agent_store(slots + (size_t)w * ND + threadIdx.x, 0.0);
+    Ms[threadIdx.x] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double ga = 0.0;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      ga += (double)a.dirs[d * ND + i] * Ms[i];
+      a.grad_dirs[d * ND + i] = (float)((double)a.alpha[d] * Ms[i]);
+    }
+    a.grad_alpha[d] = (float)ga;
+  }
+}
+
+int64_t height_blocks(const HeightGeom& g, int cus) {
+  int64_t b = (int64_t)cus * 8;
+  if (b > g.ntiles) b = g.ntiles;
+  return b < 1 ? 1 : b;
+}
+
+}  // namespace
+
+hipError_t launch_height(const HeightArgs& a, hipStream_t s) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const HeightGeom g = height_geom(a);
+  const size_t lds = (size_t)a.D * (a.nd + 1) * sizeof(float);
+  const void* k = a.nd == 3 ? reinterpret_cast<const void*>(height_kernel<3>)
+                            : reinterpret_cast<const void*>(height_kernel<2>);
+  if (lds > 64 * 1024) {
+    e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const unsigned nb = (unsigned)height_blocks(g, di.cus);
+  if (a.nd == 3)
+    hipLaunchKernelGGL(height_kernel<3>, dim3(nb), dim3(kHNT), lds, s, a);
+  else
+    hipLaunchKernelGGL(height_kernel<2>, dim3(nb), dim3(kHNT), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_height_bwd(const HeightArgs& a, hipStream_t s) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const HeightGeom g = height_geom(a);
+  if (a.grad_grid) {
+    int64_t nb = (g.nvox + kHNT - 1) / kHNT;
+    if (nb > (int64_t)di.cus * 16) nb = (int64_t)di.cus * 16;
+    hipLaunchKernelGGL(height_grid_grad_kernel, dim3((unsigned)nb), dim3(kHNT), 0, s, a, g.nvox);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.grad_dirs) {
+    const dim3 grid((unsigned)height_moment_blocks(a.D), (unsigned)a.D);
+    if (a.nd == 3)
+      hipLaunchKernelGGL(height_moments_kernel<3>, grid, dim3(kHNT), 0, s, a);
+    else
+      hipLaunchKernelGGL(height_moments_kernel<2>, grid, dim3(kHNT), 0, s, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace ecc

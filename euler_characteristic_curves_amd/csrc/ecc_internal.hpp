@@ -76,6 +76,34 @@ struct GradArgs {
   int64_t tau_stride = 0;
 };
 
+// Directional heights f_d = X + alpha_d <u_d, p> and their backward.
+struct HeightArgs {
+  const float* grid;   // forward input X
+  int nd;              // 2 or 3
+  int64_t nz, ny, nx;  // nz = 1 for 2D
+  const float* dirs;   // [D][nd], axis order slowest first
+  const float* alpha;  // [D]
+  int D;
+  float* out;          // forward: [D][voxels]
+  const float* grad_h; // backward: dL/df, [D][voxels]
+  float* grad_grid;    // [voxels] or null
+  float* grad_dirs;    // [D][nd] (with grad_alpha) or null
+  float* grad_alpha;   // [D]
+  void* ws;
+};
+
+// Moments workspace: [D tickets, padded | D x blocks x nd float64 slots].
+__host__ __device__ inline size_t height_ws_header(int D) {
+  return ((size_t)D * sizeof(unsigned int) + 255) & ~(size_t)255;
+}
+__host__ __device__ inline int height_moment_blocks(int D) {
+  const int b = (4096 + D - 1) / D;
+  return b > 1024 ? 1024 : (b < 1 ? 1 : b);
+}
+inline size_t height_workspace_bytes(int nd, int D) {
+  return height_ws_header(D) + (size_t)D * height_moment_blocks(D) * nd * sizeof(double);
+}
+
 // Largest number of grids in one launch (the workgroup grid's y extent).
 constexpr int64_t kMaxBatchPerLaunch = 65535;
 
@@ -95,5 +123,7 @@ hipError_t device_info(DeviceInfo* info);
 hipError_t launch_hard(const HardArgs& a, hipStream_t stream);
 hipError_t launch_soft(const SoftArgs& a, hipStream_t stream);
 hipError_t launch_soft_grad(const GradArgs& a, hipStream_t stream);
+hipError_t launch_height(const HeightArgs& a, hipStream_t stream);
+hipError_t launch_height_bwd(const HeightArgs& a, hipStream_t stream);
 
 }  // namespace ecc

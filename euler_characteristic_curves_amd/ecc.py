@@ -358,3 +358,91 @@ class SoftECCBatched(torch.autograd.Function):
 def soft_ecc_batched(grids, tau, lam):
     """Soft ECC of a batch of grids as an autograd op (differentiable in grids and tau)."""
     return SoftECCBatched.apply(grids, tau, lam)
+
+
+# ----------------------------------------------------- directional heights
+def _height_args(grid, dirs, alpha):
+    _dev_tensor(grid, "grid", torch.float32)
+    if grid.dim() not in (2, 3):
+        raise ValueError("grid must be 2D or 3D")
+    _dev_tensor(dirs, "dirs", torch.float32, grid.device)
+    _dev_tensor(alpha, "alpha", torch.float32, grid.device)
+    if dirs.dim() != 2 or dirs.shape[1] != grid.dim():
+        raise ValueError("dirs must be [D, grid.dim()]")
+    D = dirs.shape[0]
+    if tuple(alpha.shape) != (D,):
+        raise ValueError("alpha must be [D]")
+    return D, _shape_arr(grid)
+
+
+def ecc_height(grid, dirs, alpha, out=None):
+    """Heights grid + alpha[d] * <dirs[d], p>: float32[D, *grid.shape] (see include/ecc.h)."""
+    D, shp = _height_args(grid, dirs, alpha)
+    if out is None:
+        out = torch.empty((D,) + tuple(grid.shape), dtype=torch.float32, device=grid.device)
+    _dev_tensor(out, "out", torch.float32, grid.device)
+    if tuple(out.shape) != (D,) + tuple(grid.shape):
+        raise ValueError("out must be [D, *grid.shape]")
+    s = _stream(grid)
+    check(lib.ecc_height(_ptr(grid), grid.dim(), ctypes.cast(shp, ctypes.c_void_p), _ptr(dirs), _ptr(alpha), D,
+                         _ptr(out), ctypes.c_void_p(s.cuda_stream)), "ecc_height")
+    return out
+
+
+def ecc_height_bwd(grad_h, dirs, alpha, need_grid=True, need_dirs=True):
+    """(dL/dgrid, dL/ddirs, dL/dalpha) from dL/dheights [D, *shape]; None where not needed."""
+    _dev_tensor(grad_h, "grad_h", torch.float32)
+    if grad_h.dim() not in (3, 4):
+        raise ValueError("grad_h must be [D, *grid.shape]")
+    _dev_tensor(dirs, "dirs", torch.float32, grad_h.device)
+    _dev_tensor(alpha, "alpha", torch.float32, grad_h.device)
+    D, nd = grad_h.shape[0], grad_h.dim() - 1
+    if tuple(dirs.shape) != (D, nd) or tuple(alpha.shape) != (D,):
+        raise ValueError("dirs must be [D, ndim] and alpha [D]")
+    shp = (ctypes.c_int64 * nd)(*grad_h.shape[1:])
+    dev = grad_h.device
+    gg = torch.empty(tuple(grad_h.shape[1:]), dtype=torch.float32, device=dev) if need_grid else None
+    gd = torch.empty((D, nd), dtype=torch.float32, device=dev) if need_dirs else None
+    ga = torch.empty((D,), dtype=torch.float32, device=dev) if need_dirs else None
+    s = _stream(grad_h)
+    nb = int(lib.ecc_height_workspace_bytes(nd, D))
+    ws = get_workspace(nb, dev, s)
+    null = ctypes.c_void_p(0)
+    check(lib.ecc_height_bwd(_ptr(grad_h), nd, ctypes.cast(shp, ctypes.c_void_p), _ptr(dirs), _ptr(alpha), D,
+                             _ptr(gg) if gg is not None else null, _ptr(gd) if gd is not None else null,
+                             _ptr(ga) if ga is not None else null, _ptr(ws), ws.numel() * ws.element_size(),
+                             ctypes.c_void_p(s.cuda_stream)), "ecc_height_bwd")
+    return gg, gd, ga
+
+
+class Heights(torch.autograd.Function):
+    """Directional heights as an autograd op: (grid, dirs [D, nd], alpha [D]) -> [D, *grid.shape]."""
+
+    @staticmethod
+    def forward(ctx, grid, dirs, alpha):
+        ctx.save_for_backward(dirs, alpha)
+        return ecc_height(grid.detach().contiguous(), dirs.detach().contiguous(), alpha.detach().contiguous())
+
+    @staticmethod
+    def backward(ctx, grad_h):
+        dirs, alpha = ctx.saved_tensors
+        need_dirs = ctx.needs_input_grad[1] or ctx.needs_input_grad[2]
+        gg, gd, ga = ecc_height_bwd(grad_h.contiguous(), dirs.detach().contiguous(), alpha.detach().contiguous(),
+                                    need_grid=ctx.needs_input_grad[0], need_dirs=need_dirs)
+        return gg, gd if ctx.needs_input_grad[1] else None, ga if ctx.needs_input_grad[2] else None
+
+
+def directional_heights(grid, dirs, alpha):
+    """Heights f[d] = grid + alpha[d] <dirs[d], p>, differentiable in all three inputs."""
+    return Heights.apply(grid, dirs, alpha)
+
+
+def ecc_hard_directional(grid, dirs, alpha, tau):
+    """Hard curves of the D directional height grids: int64[D, H]."""
+    return ecc_hard_batched(ecc_height(grid, dirs, alpha), tau)
+
+
+def soft_ecc_directional(grid, dirs, alpha, tau, lam):
+    """Soft curves of the D directional height grids, float32[D, H], differentiable
+    in the grid, the directions, the scales and the thresholds."""
+    return soft_ecc_batched(directional_heights(grid, dirs, alpha), tau, lam)

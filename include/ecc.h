@@ -60,6 +60,7 @@ extern "C" {
 #define ECC_E_LAMBDA 5    /* lambda not finite or <= 0                        */
 #define ECC_E_WORKSPACE 6 /* ws is NULL or ws_bytes is too small              */
 #define ECC_E_HIP 7       /* the HIP runtime reported an error               */
+#define ECC_E_NDIRS 8     /* D < 1 or D > ECC_MAX_DIRECTIONS                  */
 
 /* grid element types */
 #define ECC_U8 0
@@ -72,6 +73,8 @@ extern "C" {
 
 #define ECC_MAX_THRESHOLDS 8192
 #define ECC_MAX_VOXELS (((int64_t)1) << 40)
+#define ECC_MAX_DIRECTIONS 4096
+#define ECC_MAX_AXIS (((int64_t)1) << 24) /* per axis, for the directional heights */
 
 /*
  * Hard ECC of a 2D grid (full-sweep kernel).
@@ -198,6 +201,47 @@ int ecc_soft_bwd_tau_batched(const float* grid, int32_t ndim, const int64_t* sha
 int ecc_soft_bwd_grid_batched(const float* grid, int32_t ndim, const int64_t* shape, int64_t batch,
                               const float* tau, int64_t tau_stride, int32_t H, float lambda,
                               const float* grad_out, float* grad_grid, void* stream);
+
+/*
+ * Directional heights (single- and multi-direction curves).
+ *   grid   device float32, ndim in {2,3}, shape[ndim] (HOST array); each axis <= 2^24
+ *   dirs   device float32[D][ndim]: direction u_d, axis order slowest first
+ *   alpha  device float32[D]: scale alpha_d
+ *   out    device float32[D][shape...]: out[d][p] = grid[p] + alpha_d * <u_d, p>,
+ *          p the integer voxel index, computed in float32 as
+ *          h = (u_0 p_0 + u_1 p_1) [+ u_2 p_2], out = grid + alpha * h, each
+ *          product and sum rounded in that order (no fused multiply-add).
+ * The page's differentiable layer has a learnable direction u and scale alpha
+ * for its single-direction version, and the multi-direction transform is its
+ * complete form ("Method / Key designs / differentiable ECC layer",
+ * "Limitations and outlook"); the page leaves the height on a grid open, and
+ * this is the reading taken: intensity plus a linear ramp.  Voxels at +inf
+ * never enter any sublevel set, so grid = 0 on a shape and +inf off it gives
+ * the shape's directional filtration.  The curves of direction d are those of
+ * out[d], e.g. from ecc_hard_2d/3d_batched or ecc_soft_fwd_batched with
+ * batch = D.  One kernel launch; no workspace.
+ */
+int ecc_height(const float* grid, int32_t ndim, const int64_t* shape, const float* dirs, const float* alpha,
+               int32_t D, float* out, void* stream);
+
+/*
+ * Backward of ecc_height.  grad_h: device float32[D][shape...] = dL/dout.
+ *   grad_grid   device float32[shape...] or NULL: sum over d of grad_h[d]
+ *               (float32, d increasing)
+ *   grad_dirs   device float32[D][ndim] or NULL: alpha_d * M[d][i],
+ *   grad_alpha  device float32[D] or NULL (both or neither): sum_i u_d,i M[d][i],
+ *               with M[d][i] = sum_p grad_h[d][p] * p_i in float64, summed in a
+ *               fixed order (the result does not depend on scheduling).
+ *   ws          device workspace of ecc_height_workspace_bytes(ndim, D) bytes
+ *               (needed with grad_dirs; zero-filled convention as above).
+ * Up to two kernel launches (one per requested output kind).
+ */
+int ecc_height_bwd(const float* grad_h, int32_t ndim, const int64_t* shape, const float* dirs, const float* alpha,
+                   int32_t D, float* grad_grid, float* grad_dirs, float* grad_alpha, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Workspace bytes of ecc_height_bwd (0 for invalid arguments). */
+size_t ecc_height_workspace_bytes(int32_t ndim, int32_t D);
 
 /*
  * Bytes of workspace needed by an operation (ECC_OP_*) for a grid of `ndim`

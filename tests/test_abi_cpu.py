@@ -29,6 +29,7 @@ def test_header_declares_expected_entry_points():
         "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
         "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
         "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_grid_batched",
+        "ecc_height", "ecc_height_bwd", "ecc_height_workspace_bytes",
         "ecc_workspace_bytes", "ecc_workspace_bytes_batched", "ecc_status_string", "ecc_last_error",
         "ecc_version"])
 
@@ -48,7 +49,7 @@ def test_header_constants_match_binding(L):
 
 
 def test_status_strings_and_version(L):
-    for code in range(8):
+    for code in range(9):
         s = L.lib.ecc_status_string(code)
         assert s and s != b"unknown status"
     assert L.lib.ecc_status_string(99) == b"unknown status"
@@ -198,6 +199,33 @@ def test_soft_batched_argument_errors(L, which):
     if which != "bwd_grid":
         assert call(ws=None) == L.ECC_E_WORKSPACE
         assert call(wsb=L.lib.ecc_workspace_bytes_batched(1, 2, 4) - 1) == L.ECC_E_WORKSPACE
+
+
+def test_height_argument_errors(L):
+    def fwd(shape=(4, 5), D=2, grid=FAKE, dirs=FAKE, alpha=FAKE, out=FAKE):
+        arr = (ctypes.c_int64 * len(shape))(*shape)
+        return L.lib.ecc_height(grid, len(shape), ctypes.cast(arr, ctypes.c_void_p), dirs, alpha, D, out, None)
+
+    def bwd(shape=(4, 5), D=2, gg=FAKE, gd=FAKE, ga=FAKE, ws=FAKE, wsb=1 << 30):
+        arr = (ctypes.c_int64 * len(shape))(*shape)
+        return L.lib.ecc_height_bwd(FAKE, len(shape), ctypes.cast(arr, ctypes.c_void_p), FAKE, FAKE, D, gg, gd, ga,
+                                    ws, wsb, None)
+    assert fwd(grid=None) == L.ECC_E_NULL
+    assert fwd(dirs=None) == L.ECC_E_NULL
+    assert fwd(alpha=None) == L.ECC_E_NULL
+    assert fwd(out=None) == L.ECC_E_NULL
+    assert fwd(shape=(2, 2, 2, 2)) == L.ECC_E_SHAPE
+    assert fwd(shape=(0, 5)) == L.ECC_E_SHAPE
+    assert fwd(shape=(3, (1 << 24) + 1)) == L.ECC_E_SHAPE
+    assert fwd(D=0) == L.ECC_E_NDIRS
+    assert fwd(D=4097) == L.ECC_E_NDIRS
+    assert fwd(shape=(1 << 20, 1 << 20), D=2) == L.ECC_E_SHAPE
+    assert bwd(gg=None, gd=None, ga=None) == L.ECC_E_NULL
+    assert bwd(ga=None) == L.ECC_E_NULL
+    assert bwd(ws=None) == L.ECC_E_WORKSPACE
+    assert bwd(wsb=L.lib.ecc_height_workspace_bytes(2, 2) - 1) == L.ECC_E_WORKSPACE
+    assert L.lib.ecc_height_workspace_bytes(4, 2) == 0 and L.lib.ecc_height_workspace_bytes(2, 0) == 0
+    assert L.lib.ecc_height_workspace_bytes(3, 4096) > 0
 
 
 def test_binding_rejects_cpu_tensors():
