@@ -11,7 +11,8 @@ Also reported on the same JSON line: per-kernel durations (mean of
 back-to-back launches, and min / median of individually timed launches, HIP
 events on the launch stream) and the roofline of each hard kernel; the other
 grid sizes (128^2, 1024^2, 1024^3) as context, the first two also as batches
-of 1024 and 64 grids in one call; the soft forward and its
+of 1024 and 64 grids in one call, and curves of a 128^3 grid along 64 / 16
+directions (hard / soft with all gradients); the soft forward and its
 backward with respect to the thresholds and to the grid at 256^3 (H=256,
 lambda=50) with their VALU-issue fraction; and the CPU oracle
 timed on a bounded sample of the same workloads (cpu_baseline), on one core
@@ -271,6 +272,57 @@ def cpu_baseline(W, g3, t3, g4, t4):
     }
 
 
+def directional_context(torch, E, W, dev, reps):
+    """Curves of a 128^3 float32 uniform grid along many directions: heights
+    f_d = X + <u_d, p> (HBM-bound elementwise kernel), then the hard curves of
+    all D height grids in one batched call (64 directions, H=256), and the soft
+    curves with every gradient (16 directions, H=128, lambda=20)."""
+    rng = np.random.default_rng(77)
+    X = W.uniform_f32((128, 128, 128), 78)
+    dX = torch.from_numpy(X).to(dev)
+    out = {}
+    for D, soft in ((64, False), (16, True)):
+        U = rng.normal(size=(D, 3))
+        U = (U / np.linalg.norm(U, axis=1, keepdims=True)).astype(np.float32)
+        dU = torch.from_numpy(U).to(dev)
+        dA = torch.ones(D, dtype=torch.float32, device=dev)
+        f = E.ecc_height(dX, dU, dA)
+        lo, hi = float(f.min().item()), float(f.max().item())
+        ms_h = timed(torch, lambda i: E.ecc_height(dX, dU, dA, out=f), reps)
+        bytes_h = X.size * 4 * (1 + D)
+        rec = {"directions": D, "height_ms": ms_h, "height_GB_s": bytes_h / (ms_h * 1e-3) / 1e9,
+               "height_frac_hbm_peak": bytes_h / (ms_h * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        if not soft:
+            tau = torch.from_numpy(W.tau_linspace(lo, hi, 256)).to(dev)
+            o = torch.empty((D, 256), dtype=torch.int64, device=dev)
+            ms_c = timed(torch, lambda i: E.ecc_hard_batched(f, tau, out=o), reps)
+            rec.update({"H": 256, "hard_curves_ms": ms_c, "total_ms": ms_h + ms_c,
+                        "voxel_directions_per_s": X.size * D / ((ms_h + ms_c) * 1e-3)})
+            out["hard"] = rec
+        else:
+            tau = torch.from_numpy(W.tau_linspace(lo, hi, 128)).to(dev)
+            w = torch.from_numpy(rng.standard_normal((D, 128)).astype(np.float32)).to(dev)
+            xg = dX.clone().requires_grad_(True)
+            ug = dU.clone().requires_grad_(True)
+            ag = dA.clone().requires_grad_(True)
+            tg = tau.clone().requires_grad_(True)
+
+            def step(i):
+                S = E.soft_ecc_directional(xg, ug, ag, tg, 20.0)
+                (S * w).sum().backward()
+
+            for i in range(3):  # the first backward passes load torch's gradient-accumulation kernels
+                step(i)
+            ms_fb = timed(torch, step, max(3, reps // 5))
+            ms_fw = timed(torch, lambda i: E.soft_ecc_directional(dX, dU, dA, tau, 20.0), max(3, reps // 5))
+            rec.update({"H": 128, "lambda": 20.0, "soft_forward_ms": ms_fw, "soft_forward_backward_ms": ms_fb})
+            out["soft"] = rec
+        del f
+    del dX
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -373,6 +425,7 @@ def main():
                 del gb, ob
             del dg, dtau, o
             torch.cuda.empty_cache()
+        context["directional_128cube"] = directional_context(torch, E, W, dev, args.kernel_reps)
 
     soft = None
     if not args.no_soft:
