@@ -95,6 +95,68 @@ __global__ __launch_bounds__(kHNT) void height_kernel(HeightArgs a) {
   }
 }
 
+// Coordinates of a thread's current voxel along a grid-stride walk: one
+// division at the start, then a mixed-radix add of the stride per step.
+struct Walk {
+  int64_t x, y, z, sx, sy, sz, nx, ny;
+  __device__ void init(int64_t idx, int64_t stride, int64_t nx_, int64_t ny_) {
+    nx = nx_;
+    ny = ny_;
+    const int64_t r = idx / nx, rs = stride / nx;
+    x = idx - r * nx;
+    z = r / ny;
+    y = r - z * ny;
+    sx = stride - rs * nx;
+    sz = rs / ny;
+    sy = rs - sz * ny;
+  }
+  __device__ void step() {
+    x += sx;
+    y += sy;
+    if (x >= nx) {
+      x -= nx;
+      ++y;
+    }
+    z += sz;
+    if (y >= ny) {
+      y -= ny;
+      ++z;
+    }
+  }
+};
+
+// Rows of a multiple of 4 voxels with 16-byte aligned grid and output:
+// every thread takes 4 consecutive voxels of the flattened grid (one row, as
+// nx is a multiple of 4) and writes one float4 per direction, so narrow rows
+// keep every lane busy and stores are 16 bytes wide.
+template <int ND>
+__global__ __launch_bounds__(kHNT) void height_vec_kernel(HeightArgs a, int64_t nquads) {
+  extern __shared__ float sd[];  // u[D][ND] then alpha[D]
+  const int D = a.D;
+  for (int i = threadIdx.x; i < D * (ND + 1); i += kHNT) sd[i] = i < D * ND ? a.dirs[i] : a.alpha[i - D * ND];
+  __syncthreads();
+  const int64_t nvox = a.nz * a.ny * a.nx;
+  const int64_t stride = (int64_t)gridDim.x * kHNT;
+  const int64_t q0 = (int64_t)blockIdx.x * kHNT + threadIdx.x;
+  Walk w;
+  w.init(4 * q0, 4 * stride, a.nx, a.ny);
+  for (int64_t q = q0; q < nquads; q += stride, w.step()) {
+    const int64_t idx = 4 * q, x0 = w.x;
+    const float4 X = *reinterpret_cast<const float4*>(a.grid + idx);
+    const float pz = (float)(ND == 3 ? w.z : 0), py = (float)w.y;
+    for (int d = 0; d < D; ++d) {
+      const float* u = sd + d * ND;
+      const float al = sd[D * ND + d];
+      float4 f;
+      f.x = height_of<ND>(X.x, al, u, pz, py, (float)(x0 + 0));
+      f.y = height_of<ND>(X.y, al, u, pz, py, (float)(x0 + 1));
+      f.z = height_of<ND>(X.z, al, u, pz, py, (float)(x0 + 2));
+      f.w = height_of<ND>(X.w, al, u, pz, py, (float)(x0 + 3));
+      *reinterpret_cast<float4*>(a.out + (size_t)d * (size_t)nvox + idx) = f;
+    }
+  }
+}
+
 // dL/dX = sum over directions, float32 in increasing d.
 __global__ __launch_bounds__(kHNT) void height_grid_grad_kernel(HeightArgs a, int64_t nvox) {
   const int64_t stride = (int64_t)gridDim.x * kHNT;
@@ -111,8 +173,10 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// Moments of direction blockIdx.y, then dL/du and dL/dalpha by its last workgroup.
-template <int ND>
+// Moments of direction blockIdx.y, then dL/du and dL/dalpha by its last
+// workgroup.  VEC: rows of a multiple of 4 voxels, 16-byte aligned, read as
+// float4 quads along a grid-stride walk; otherwise row tiles.
+template <int ND, bool VEC>
 __global__ __launch_bounds__(kHNT) void height_moments_kernel(HeightArgs a) {
   __shared__ double red[kHNT / 64][ND];
   __shared__ double Ms[ND];
@@ -123,20 +187,8 @@ __global__ __launch_bounds__(kHNT) void height_moments_kernel(HeightArgs a) {
   double m[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) m[i] = 0.0;
-  for (int64_t t = blockIdx.x; t < g.ntiles; t += gridDim.x) {
-    const int64_t row = t / g.ntx, xc = t - row * g.ntx;
-    const int64_t z = ND == 3 ? row / g.n1 : 0, y = row - z * g.n1;
-    double sx = 0.0, s = 0.0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t x = xc * kHTileX + j * kHNT + threadIdx.x;
-      if (x < g.nx) {
-        const double v = (double)G[row * g.nx + x];
-        s += v;
-        sx = fma(v, (double)x, sx);
-      }
-    }
-    // the row's voxels share z and y
+  // the voxels of one quad or one row share z and y
+  auto add = [&](double s, double sx, int64_t z, int64_t y) {
     if constexpr (ND == 3) {
       m[0] = fma(s, (double)z, m[0]);
       m[1] = fma(s, (double)y, m[1]);
@@ -144,6 +196,35 @@ __global__ __launch_bounds__(kHNT) void height_moments_kernel(HeightArgs a) {
     } else {
       m[0] = fma(s, (double)y, m[0]);
       m[1] += sx;
+    }
+  };
+  if constexpr (VEC) {
+    const int64_t nquads = g.nvox / 4, stride = (int64_t)gridDim.x * kHNT;
+    const int64_t q0 = (int64_t)blockIdx.x * kHNT + threadIdx.x;
+    Walk w;
+    w.init(4 * q0, 4 * stride, g.nx, g.n1);
+    for (int64_t q = q0; q < nquads; q += stride, w.step()) {
+      const float4 v = *reinterpret_cast<const float4*>(G + 4 * q);
+      const double x = (double)w.x;
+      const double s = ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
+      const double sx = fma((double)v.x, x, fma((double)v.y, x + 1.0, fma((double)v.z, x + 2.0, (double)v.w * (x + 3.0))));
+      add(s, sx, w.z, w.y);
+    }
+  } else {
+    for (int64_t t = blockIdx.x; t < g.ntiles; t += gridDim.x) {
+      const int64_t row = t / g.ntx, xc = t - row * g.ntx;
+      const int64_t z = ND == 3 ? row / g.n1 : 0, y = row - z * g.n1;
+      double sx = 0.0, s = 0.0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t x = xc * kHTileX + j * kHNT + threadIdx.x;
+        if (x < g.nx) {
+          const double v = (double)G[row * g.nx + x];
+          s += v;
+          sx = fma(v, (double)x, sx);
+        }
+      }
+      add(s, sx, z, y);
     }
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -210,6 +291,24 @@ hipError_t launch_height(const HeightArgs& a, hipStream_t s) {
     e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
+  const bool vec = a.nx % 4 == 0 && reinterpret_cast<uintptr_t>(a.grid) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.out) % 16 == 0;
+  if (vec) {
+    const void* kv = a.nd == 3 ? reinterpret_cast<const void*>(height_vec_kernel<3>)
+                               : reinterpret_cast<const void*>(height_vec_kernel<2>);
+    if (lds > 64 * 1024) {
+      e = hipFuncSetAttribute(kv, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    const int64_t nquads = g.nvox / 4;
+    int64_t nb = (nquads + kHNT - 1) / kHNT;
+    if (nb > (int64_t)di.cus * 8) nb = (int64_t)di.cus * 8;
+    if (a.nd == 3)
+      hipLaunchKernelGGL(height_vec_kernel<3>, dim3((unsigned)nb), dim3(kHNT), lds, s, a, nquads);
+    else
+      hipLaunchKernelGGL(height_vec_kernel<2>, dim3((unsigned)nb), dim3(kHNT), lds, s, a, nquads);
+    return hipGetLastError();
+  }
   const unsigned nb = (unsigned)height_blocks(g, di.cus);
   if (a.nd == 3)
     hipLaunchKernelGGL(height_kernel<3>, dim3(nb), dim3(kHNT), lds, s, a);
@@ -232,10 +331,18 @@ hipError_t launch_height_bwd(const HeightArgs& a, hipStream_t s) {
   }
   if (a.grad_dirs) {
     const dim3 grid((unsigned)height_moment_blocks(a.D), (unsigned)a.D);
-    if (a.nd == 3)
-      hipLaunchKernelGGL(height_moments_kernel<3>, grid, dim3(kHNT), 0, s, a);
-    else
-      hipLaunchKernelGGL(height_moments_kernel<2>, grid, dim3(kHNT), 0, s, a);
+    const bool vec = a.nx % 4 == 0 && reinterpret_cast<uintptr_t>(a.grad_h) % 16 == 0;
+    if (a.nd == 3) {
+      if (vec)
+        hipLaunchKernelGGL((height_moments_kernel<3, true>), grid, dim3(kHNT), 0, s, a);
+      else
+        hipLaunchKernelGGL((height_moments_kernel<3, false>), grid, dim3(kHNT), 0, s, a);
+    } else {
+      if (vec)
+        hipLaunchKernelGGL((height_moments_kernel<2, true>), grid, dim3(kHNT), 0, s, a);
+      else
+        hipLaunchKernelGGL((height_moments_kernel<2, false>), grid, dim3(kHNT), 0, s, a);
+    }
     e = hipGetLastError();
   }
   return e;

@@ -43,7 +43,8 @@ def _case(shape, D, seed, with_inf=False):
     return X, U, A
 
 
-@pytest.mark.parametrize("shape", [(1, 1), (7, 5), (33, 1030), (1, 1, 1), (3, 7, 1100), (17, 19, 23)])
+@pytest.mark.parametrize("shape", [(1, 1), (7, 5), (33, 1030), (16, 64), (1, 4), (1, 1, 1), (3, 7, 1100),
+                                   (17, 19, 23), (5, 6, 128), (2, 3, 4)])
 @pytest.mark.parametrize("D", [1, 3, 17])
 def test_heights_bit_exact(E, shape, D):
     import torch
@@ -101,7 +102,8 @@ def _moment_close(got, want, mag):
     return np.nonzero(~(err <= tol))[0], float(np.max(err / tol)) if err.size else 0.0
 
 
-@pytest.mark.parametrize("shape", [(1, 1), (31, 47), (130, 70), (9, 17, 33), (40, 41, 42)])
+@pytest.mark.parametrize("shape", [(1, 1), (31, 47), (130, 70), (64, 128), (1, 4), (9, 17, 33), (40, 41, 42),
+                                   (10, 12, 16), (3, 5, 4)])
 @pytest.mark.parametrize("D", [1, 5])
 def test_height_bwd(E, shape, D):
     import torch
@@ -127,7 +129,7 @@ def test_height_bwd(E, shape, D):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("shape", [(48, 50), (20, 21, 22)])
+@pytest.mark.parametrize("shape", [(48, 50), (40, 64), (20, 21, 22), (16, 20, 24)])
 def test_soft_directional_forward_and_gradients(E, shape):
     """Soft curves of D directions and the gradients of all four inputs,
     through the autograd chain heights -> batched soft curves."""
