@@ -417,8 +417,8 @@ def test_batched_oracle_is_per_grid():
     rows = oracle.ecc_hard_batched(g, per)
     for b in range(5):
         assert rows[b].tolist() == [pins.brute_chi(g[b], float(t)) for t in per[b]]
-    # all grids at their max: each contributes 1, while the 3D stack is one box (also 1),
-    # but below the max the 3D stack joins grids through z-edges
+    # the rows do not add up to the curve of the stacked 3D grid, whose cells
+    # join neighbouring grids along z
     assert not np.array_equal(oracle.ecc_hard_batched(g, tau).sum(0), oracle.ecc_hard(g, tau))
 
 
