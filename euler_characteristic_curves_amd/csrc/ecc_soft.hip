@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles
         for (int base = tb; base < te; base += kLaneGroups) {
           const Term tm = term(base);
           const double wd = (double)tm.w;
-          const float wf = tm.w * tm.a;
+          const double wfd = wd * (double)tm.a;  // w F, once per term
 #pragma unroll
           for (int r = 0; r < kSlots; ++r) {
             const float d = fmaf(tm.a, e[r], 1.0f);
@@ -219,8 +219,9 @@ __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles
             if constexpr (!BWD) {
               acc[r] = fma(wd, (double)rr, acc[r]);
             } else {
-              const float q = (wf * rr) * (e[r] * rr);  // w t s^2 = w s (1 - s), t = F E
-              acc[r] += (double)q;
+              // w s (1 - s) = w t s^2 = (w F) (E s) s, t = F E
+              const float q = (e[r] * rr) * rr;
+              acc[r] = fma(wfd, (double)q, acc[r]);
             }
           }
         }
@@ -236,8 +237,8 @@ __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles
             if constexpr (!BWD) {
               acc[r] = fma(wd, (double)rr, acc[r]);
             } else {
-              const float q = (tm.w * (tt * rr)) * rr;
-              acc[r] += (double)q;
+              const float q = (tt * rr) * rr;
+              acc[r] = fma(wd, (double)q, acc[r]);
             }
           }
         }
