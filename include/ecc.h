@@ -29,7 +29,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work and return; outputs are valid once the stream reaches
  *     that point.  Calls that share one workspace must not overlap in time.
- *   - Workspace: `ws` must hold ecc_workspace_bytes(...) bytes.  Before its
+ *   - Workspace: `ws` must hold the bytes its size function gives
+ *     (ecc_workspace_bytes, ecc_workspace_bytes_batched or
+ *     ecc_height_workspace_bytes for the call).  Before its
  *     FIRST use it must be zero-filled by the caller (e.g. torch.zeros);
  *     every call leaves it zero-filled again when it completes, so it can be
  *     reused by the next call on the same stream without clearing.
@@ -38,8 +40,9 @@
  *     failure returns ECC_E_HIP.  ecc_last_error() returns a thread-local
  *     message for the last failing call.  Nothing is printed and no C++
  *     exception crosses the ABI.
- *   - Not checked (documented preconditions): grid values are finite (NaN
- *     is unspecified); buffers are large enough for the shape given.
+ *   - Not checked (documented preconditions): no grid value is NaN (+-inf
+ *     are ordered like any other value: a cell at +inf enters only at a
+ *     threshold of +inf); buffers are large enough for the shape given.
  */
 #ifndef ECC_MI355_H
 #define ECC_MI355_H
