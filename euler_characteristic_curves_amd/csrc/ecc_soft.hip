@@ -9,15 +9,17 @@
 // evaluated by custom forward / backward kernels.  Cells and values are those
 // of the hard curve (max of corners, V-construction).
 //
-// Work split (cells x thresholds).  Each workgroup takes tiles of 1024 voxels.
+// Work split (cells x thresholds).  Each workgroup takes tiles of 512 voxels.
 // Phase A turns a tile into a short list of (value, weight) terms: the same
 // exact regrouping as the hard kernels (four row sequences per voxel,
 // telescoped along x, equal values merged), so a term carries the summed sign
 // of every cell that has that value.  Phase B sweeps the list in LDS against
-// the thresholds: every wave takes a quarter of the terms, four at a time
-// (one per 16-lane group), and every lane owns 16 thresholds of each
-// 256-threshold chunk, so one broadcast LDS read of a term feeds 16 sigmoids
-// per lane and the sweep's LDS traffic stays well below its VALU work.  The
+// the thresholds: every wave takes a quarter of the terms, two at a time
+// (one per half-wave), and every lane owns 8 thresholds of each
+// 256-threshold chunk, so one broadcast LDS read of a term feeds 8 sigmoids
+// per lane and the sweep's LDS traffic stays well below its VALU work.
+// Tiles of 512 voxels and 8 thresholds per lane keep LDS and registers at
+// 7 workgroups per CU, enough waves to hide the latency of the sweep.  The
 // sigmoid costs one FMA and one
 // reciprocal per (term, threshold) in the factored form
 //     exp(lambda (v - tau)) = 2^{L (v - c)} * 2^{L (c - tau)},  L = lambda log2 e,
@@ -36,10 +38,10 @@
 namespace ecc {
 namespace {
 
-constexpr int kTileVox = 1024;          // voxels per tile
+constexpr int kTileVox = 512;           // voxels per tile
 constexpr int kTermCap = 4 * kTileVox;  // at most 4 terms per voxel
 constexpr int kChunk = 256;             // thresholds per sweep chunk
-constexpr int kLaneGroups = 4;          // terms a wave sweeps at once
+constexpr int kLaneGroups = 2;          // terms a wave sweeps at once
 constexpr int kGroupLanes = 64 / kLaneGroups;
 constexpr int kSlots = kChunk / kGroupLanes;  // thresholds per lane and chunk
 
@@ -275,8 +277,11 @@ hipError_t launch_soft(const SoftArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int64_t nvox = a.nz * a.ny * a.nx;
   const int64_t ntiles = (nvox + kTileVox - 1) / kTileVox;
-  // workgroups per grid: the launch's share of four per CU
-  int64_t g = ((int64_t)di.cus * 4 + a.batch - 1) / a.batch;
+  // workgroups per grid: the launch's share of 64 per CU.  Far more than fit
+  // at once (7 per CU): tiles differ in how many terms they hold, and short
+  // workgroups that the dispatcher keeps replacing balance the CUs better
+  // than a few persistent ones (256^3: 64 per CU is 11 % faster than 4).
+  int64_t g = ((int64_t)di.cus * 64 + a.batch - 1) / a.batch;
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
   // fixed point: |partial| and |total| <= #cells <= 8 * nvox, kept below 2^61
