@@ -140,18 +140,23 @@ typedef __attribute__((address_space(3))) int lds_int;
 template <int V, int C, bool ADDR = false>
 __device__ __forceinline__ void tele_add(const int (&s)[V], int left, int right, int sign, int* hist,
                                          int lofs) {
-  int inc_prev = (int)(s[0] > left);
+  // d = s(x) - s(x+1) is negative exactly when the sequence rises after x.
+  // Keys are below 2^18, so |d| < 2^24 and d >> 24 (arithmetic) is -1 on a
+  // rise and 0 otherwise: the weight inc(x) - inc(x-1) is then one
+  // subtraction of the top bytes of two differences (a byte-select form of
+  // the subtraction, no separate compare and select per update).
+  int dprev = left - s[0];
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const int nxt = j + 1 < V ? s[j + 1] : right;
-    const int inc = (int)(nxt > s[j]);
-    const int w = inc - inc_prev;
-    inc_prev = inc;
+    const int d = s[j] - nxt;
+    const int w = sign > 0 ? (dprev >> 24) - (d >> 24) : (d >> 24) - (dprev >> 24);
+    dprev = d;
     if constexpr (ADDR)
-      __hip_atomic_fetch_add((lds_int*)(size_t)(unsigned int)s[j], sign > 0 ? w : -w, __ATOMIC_RELAXED,
+      __hip_atomic_fetch_add((lds_int*)(size_t)(unsigned int)s[j], w, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_WORKGROUP);
     else
-      atomicAdd(&hist[s[j] * C + lofs], sign > 0 ? w : -w);
+      atomicAdd(&hist[s[j] * C + lofs], w);
   }
 }
 
