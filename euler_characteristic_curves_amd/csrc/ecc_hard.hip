@@ -660,6 +660,29 @@ __device__ __forceinline__ Lds setup_lds(unsigned char* smem, const HardArgs& a,
   return L;
 }
 
+// Tiles of this workgroup: t = first, first + step, ... while t < end.  The
+// dispatcher hands workgroups to the chip's 8 XCDs in turn (linear id mod 8)
+// and each XCD has its own L2.  With at least 8 workgroups, XCD x takes the
+// x-th eighth of the tile range, split over its own workgroups, so tiles
+// that are neighbours in x (and mostly in y and z) run on one XCD: the edge
+// columns and halo rows that each reads from the other come from that XCD's
+// L2 instead of HBM, and every XCD still gets an equal share of the tiles.
+// (Tile counts stay far below 2^31: a tile holds at least 256 voxels.)
+struct TileRange {
+  int first, end, step;
+};
+
+__device__ __forceinline__ TileRange tile_range(int64_t ntiles64) {
+  constexpr int X = 8;
+  const int b = (int)blockIdx.x, g = (int)gridDim.x, ntiles = (int)ntiles64;
+  if (g < X) return TileRange{b, ntiles, g};
+  const int x = b % X, j = b / X;
+  const int nwg = g / X + (x < g % X ? 1 : 0);  // workgroups on this XCD
+  const int lo = x * (ntiles / X) + (x < ntiles % X ? x : ntiles % X);
+  const int hi = lo + ntiles / X + (x < ntiles % X ? 1 : 0);
+  return TileRange{lo + j, hi, nwg};
+}
+
 // The grid of a batch that this workgroup row works on.
 __device__ __forceinline__ void batch_slice(HardArgs& a) {
   const int64_t b = blockIdx.y;
@@ -693,7 +716,8 @@ __global__ __launch_bounds__(NT) void hard2d_kernel(HardArgs a, int nbins, int64
   // which lets the compiler schedule the unrolled row loop as a whole
   auto sweep = [&](auto thc) {
     const int64_t h = thc.value > 0 ? (int64_t)thc.value : (int64_t)th;
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    for (TileRange tr = tile_range(ntiles); tr.first < tr.end; tr.first += tr.step) {
+      const int64_t t = tr.first;
       const int64_t tx = t % ntx, tyb = t / ntx;
       const int64_t ys = (tyb * (NT / 64) + wave) * h;
       if (ys >= ny) continue;
@@ -1023,7 +1047,8 @@ __global__ __launch_bounds__(NT, MINW) void hard3d_kernel(HardArgs a, int nbins,
   constexpr int64_t CHUNK = 64 * VEC;
   const bool vok = vec_ok != 0;
 
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  for (TileRange tr = tile_range(ntiles); tr.first < tr.end; tr.first += tr.step) {
+    const int64_t t = tr.first;
     const int64_t tx = t % ntx;
     const int64_t rest = t / ntx;
     const int64_t tyg = rest % nty4, tz = rest / nty4;
@@ -1197,6 +1222,7 @@ hipError_t launch2d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   if (th < 1) th = 1;
   const int64_t nty = (a.ny + th * kWavesPerBlock - 1) / (th * kWavesPerBlock);
   const int64_t ntiles = ntx * nty;
+  if (ntiles > INT32_MAX) return hipErrorInvalidValue;  // the kernels count tiles in 32 bits
   const size_t esz = DT == 0 ? 1 : 4;
   const int vec_ok = (reinterpret_cast<uintptr_t>(a.grid) % (VEC * esz) == 0) &&
                      ((a.nx * (int64_t)esz) % (int64_t)(VEC * esz) == 0);
@@ -1234,6 +1260,7 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   if (TZ < 2 && a.nz >= 2) TZ = 2;  // a tile of one plane would re-read as many halo planes as it owns
   ntz = (a.nz + TZ - 1) / TZ;
   const int64_t ntiles = ntx * nty4 * ntz;
+  if (ntiles > INT32_MAX) return hipErrorInvalidValue;  // the kernels count tiles in 32 bits
   const size_t esz = DT == 0 ? 1 : 4;
   const int vec_ok = (reinterpret_cast<uintptr_t>(a.grid) % (VEC * esz) == 0) &&
                      ((a.nx * (int64_t)esz) % (int64_t)(VEC * esz) == 0);
