@@ -667,7 +667,8 @@ __device__ __forceinline__ Lds setup_lds(unsigned char* smem, const HardArgs& a,
 // that are neighbours in x (and mostly in y and z) run on one XCD: the edge
 // columns and halo rows that each reads from the other come from that XCD's
 // L2 instead of HBM, and every XCD still gets an equal share of the tiles.
-// (Tile counts stay far below 2^31: a tile holds at least 256 voxels.)
+// (Tile counts are 32-bit: the launchers refuse 2^31 tiles or more, which only a
+// grid of a few columns and more than 2^36 rows could need.)
 struct TileRange {
   int first, end, step;
 };
