@@ -77,6 +77,23 @@ def test_hard_random_shapes(E, shape, dtype):
         _check_hard(E, g, _taus(rng, g, H, kind), f"{dtype}-{kind}")
 
 
+@pytest.mark.parametrize("ntiles", [1, 2, 7, 8, 9, 15, 16, 17, 23, 64, 65, 127, 300])
+def test_hard_tile_counts_around_xcd_split(E, ntiles):
+    """Small grids launch one workgroup per tile; below 8 workgroups the tiles are
+    strided, from 8 up every XCD takes a contiguous share.  Tile counts around
+    multiples of 8 (with uneven shares) must still cover every tile once."""
+    rng = np.random.default_rng(zlib.crc32(repr(("tiles", ntiles)).encode()))
+    # 2D float: a 256-column chunk by four one-row wave tiles per tile
+    g = rng.random((4 * ntiles, 256), dtype=np.float32)
+    _check_hard(E, g, W.tau_linspace(0.0, 1.0, 200), f"tiles2d-{ntiles}")
+    # 2D uint8: a 1024-column chunk per tile
+    g8 = rng.integers(0, 256, size=(4 * ntiles, 1024), dtype=np.uint8)
+    _check_hard(E, g8, W.tau_integers(256), f"tiles2d-u8-{ntiles}")
+    # 3D float: a 256-column chunk, 32 rows, two planes per tile
+    g3 = rng.random((2 * ntiles, 32, 256), dtype=np.float32)
+    _check_hard(E, g3, W.tau_linspace(0.0, 1.0, 64), f"tiles3d-{ntiles}")
+
+
 @pytest.mark.parametrize("nx", [4, 16, 32, 64, 124, 128, 252, 260, 528, 1008, 1040, 1552])
 @pytest.mark.parametrize("dtype", ["u8", "f32", "f32ties"])
 def test_hard_aligned_partial_chunks(E, nx, dtype):
