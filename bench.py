@@ -154,6 +154,69 @@ def traffic_run():
     print("traffic run done: copy bytes", d4.numel() * 4, flush=True)
 
 
+def soft_sweep_terms(g):
+    """Number of (value, weight) terms the soft sweep evaluates for grid g.
+
+    Mirrors how the sweep builds its terms (measurement only; the result does
+    not enter any curve): per voxel, the four row sequences of the telescoped
+    regrouping (the row, the max over y, over z, and over y and z), each with
+    weight inc(x) - inc(x-1), signed +, -, -, +; equal values within a voxel
+    are merged, and terms of weight 0 or of cells outside the grid dropped.
+    The sweep evaluates terms x H sigmoids.
+    """
+    inf = np.float32(np.inf)
+    g = g.reshape((1,) * (3 - g.ndim) + g.shape).astype(np.float32, copy=False)
+    nz, ny, nx = g.shape
+    col = np.full((ny, 1), inf, np.float32)
+    row = np.full((1, nx), inf, np.float32)
+    total = 0
+    for z in range(nz):
+        a = g[z]
+        b = g[z + 1] if z + 1 < nz else np.full_like(a, inf)
+        ay, by = np.vstack([a[1:], row]), np.vstack([b[1:], row])
+        v = [a, np.maximum(a, ay), np.maximum(a, b), np.maximum(np.maximum(a, ay), np.maximum(b, by))]
+        w = []
+        for q, c in enumerate(v):
+            left, right = np.hstack([col, c[:, :-1]]), np.hstack([c[:, 1:], col])
+            wq = (right > c).astype(np.int32) - (c > left).astype(np.int32)
+            w.append(-wq if q in (1, 2) else wq)
+        m = v[3] == v[2]
+        w[2], w[3] = np.where(m, w[2] + w[3], w[2]), np.where(m, 0, w[3])
+        m = (v[3] == v[1]) & (w[3] != 0)
+        w[1], w[3] = np.where(m, w[1] + w[3], w[1]), np.where(m, 0, w[3])
+        m = v[2] == v[1]
+        w[1], w[2] = np.where(m, w[1] + w[2], w[1]), np.where(m, 0, w[2])
+        m = v[1] == v[0]
+        w[0], w[1] = np.where(m, w[0] + w[1], w[0]), np.where(m, 0, w[1])
+        m = v[2] == v[0]
+        w[0], w[2] = np.where(m, w[0] + w[2], w[0]), np.where(m, 0, w[2])
+        total += sum(int(np.count_nonzero((wq != 0) & (vq < inf))) for vq, wq in zip(v, w))
+    return total
+
+
+def sigmoid_ceiling(torch, cus):
+    """Measured pairs/s of the soft sweep's per-pair arithmetic with every
+    operand in registers (libecc_sigmoid_rate.so): (forward, backward)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "euler_characteristic_curves_amd", "libecc_sigmoid_rate.so"))
+    lib.ecc_sigmoid_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ecc_sigmoid_rate.restype = ctypes.c_int
+    blocks, iters = 8 * cus, 2048
+    out = torch.empty(blocks * 256, dtype=torch.float64, device="cuda:0")
+    s = torch.cuda.current_stream()
+    rates = []
+    for bwd in (0, 1):
+        def run(i):
+            st = lib.ecc_sigmoid_rate(bwd, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                      ctypes.c_void_p(s.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"ecc_sigmoid_rate failed with HIP error {st}")
+        run(0)
+        ms = min(timed(torch, run, 3) for _ in range(3))
+        rates.append(blocks * 256 * iters * 8 / (ms * 1e-3))
+    return tuple(rates)
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -450,11 +513,20 @@ def main():
         def frac(v, ms):
             return None if v is None else v / (ms * 1e-3) / VALU_WAVE_INSTR_PEAK
 
+        sig = soft_sweep_terms(gs) * ts.size
+        cf_rate, cb_rate = sigmoid_ceiling(torch, torch.cuda.get_device_properties(0).multi_processor_count)
         soft = {
             "workload": "soft ECC 256^3 float32 uniform, H=256, lambda=50",
             "fwd_ms": msf, "bwd_ms": msb, "fwd_plus_bwd_ms": msf + msb,
             "cell_threshold_pairs": pairs,
             "fwd_pairs_per_s": pairs / (msf * 1e-3), "bwd_pairs_per_s": pairs / (msb * 1e-3),
+            # sigmoids the sweep actually evaluates (merged terms x H), their
+            # rate, and the rate of the same per-pair arithmetic measured with
+            # every operand in registers on this GPU
+            "sigmoids_per_pass": sig,
+            "fwd_sigmoids_per_s": sig / (msf * 1e-3), "bwd_sigmoids_per_s": sig / (msb * 1e-3),
+            "sigmoid_ceiling_per_s": {"fwd": cf_rate, "bwd": cb_rate},
+            "sigmoid_ceiling_frac": {"fwd": sig / (msf * 1e-3) / cf_rate, "bwd": sig / (msb * 1e-3) / cb_rate},
             "bwd_grid_ms": msg,
             "bwd_grid_voxels_per_s": gs.size / (msg * 1e-3),
             "bwd_grid_nonzero_voxels": grad_nonzero,

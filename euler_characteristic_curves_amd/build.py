@@ -3,7 +3,8 @@
 Usage: ``python -m euler_characteristic_curves_amd.build`` (also called by
 ``__graft_entry__.build()``).  Sources are compiled in parallel into
 ``_build/`` at the repository root and linked into
-``euler_characteristic_curves_amd/libecc_mi355.so``.
+``euler_characteristic_curves_amd/libecc_mi355.so``.  The benchmark's
+sigmoid-rate probe is linked on its own into ``libecc_sigmoid_rate.so``.
 """
 
 import concurrent.futures as cf
@@ -20,6 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libecc_mi355.so")
 
 SOURCES = ["ecc_api.cpp", "ecc_hard.hip", "ecc_soft.hip", "ecc_soft_grad.hip", "ecc_height.hip"]
+RATE_SOURCE = "ecc_sigmoid_rate.hip"
+RATE_LIB = os.path.join(PKG, "libecc_sigmoid_rate.so")
 ARCH = os.environ.get("ECC_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [
@@ -51,19 +54,21 @@ def _compile(src):
 def build(verbose=False):
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        results = list(ex.map(_compile, SOURCES + [RATE_SOURCE]))
+    rate_obj = results.pop()[0]
     objs = [o for o, _ in results]
     if verbose:
         for _, err in results:
             if err.strip():
                 print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs), (RATE_LIB, [rate_obj])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + lib_objs
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 
