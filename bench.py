@@ -53,6 +53,7 @@ KERNEL_SOURCES = ("euler_characteristic_curves_amd/csrc/ecc_hard.hip",
                   "euler_characteristic_curves_amd/csrc/ecc_device.hpp",
                   "euler_characteristic_curves_amd/csrc/ecc_internal.hpp")
 TRAFFIC_PROFILE = "profiles/hard3d_512cube_f32_traffic.md"
+TRAFFIC_PROFILE_U8 = "profiles/hard2d_8192sq_u8_traffic.md"
 SOFT_SOURCES = ("euler_characteristic_curves_amd/csrc/ecc_soft.hip",
                 "euler_characteristic_curves_amd/csrc/ecc_soft_grad.hip",
                 "euler_characteristic_curves_amd/csrc/ecc_star.hpp",
@@ -91,14 +92,14 @@ def profile_fields(rel):
     return fields
 
 
-def recorded_traffic():
-    """HBM bytes per hard3d launch from the committed rocprofv3 --pmc profile.
+def recorded_traffic(profile=TRAFFIC_PROFILE):
+    """HBM bytes per launch of a hard kernel from its committed rocprofv3 --pmc profile.
 
     Returns None unless the profile was taken on the current kernel sources
     (its `kernel_source_sha256:` line matches), so a stale figure is never
     reported.
     """
-    fields = profile_fields(TRAFFIC_PROFILE)
+    fields = profile_fields(profile)
     if fields.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
@@ -134,7 +135,8 @@ def traffic_run():
 
     Runs a plain 512 MiB device-to-device copy (the calibration kernel of
     known size) three times, then the hard 3D kernel on the 512^3 float32
-    field three times.
+    field three times, then the hard 2D kernel on three different 8192^2
+    uint8 grids.
     """
     import torch
 
@@ -150,6 +152,13 @@ def traffic_run():
     torch.cuda.synchronize()
     for _ in range(3):
         E.ecc_hard_3d(d4, dt4)
+    torch.cuda.synchronize()
+    g3, t3, _ = W.make_workload("c3_8192sq_u8")
+    d3 = [torch.from_numpy(np.roll(g3, k, axis=0)).to(dev) for k in range(3)]
+    dt3 = torch.from_numpy(t3).to(dev)
+    torch.cuda.synchronize()
+    for k in range(3):
+        E.ecc_hard_2d(d3[k], dt3)
     torch.cuda.synchronize()
     print("traffic run done: copy bytes", d4.numel() * 4, flush=True)
 
@@ -569,6 +578,7 @@ def main():
         },
         "kernels": {
             "hard_8192sq_u8": {"ms": ms3, "min_ms": mm3[0], "median_ms": mm3[1],
+                               "traffic": recorded_traffic(TRAFFIC_PROFILE_U8),
                                "voxels_per_s": n3 / (ms3 * 1e-3), "GB_s": gbs3,
                                "frac_hbm_peak": gbs3 / HBM_PEAK_GBS, "algorithmic_bytes": alg3},
             "hard_512cube_f32": {"ms": ms4, "min_ms": mm4[0], "median_ms": mm4[1],
