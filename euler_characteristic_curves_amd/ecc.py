@@ -19,13 +19,18 @@ __all__ = [
 ]
 
 _WS = {}
+_WS_BYTES = {}
 
 
 def workspace_bytes(op, H, shape=None):
-    n = lib.ecc_workspace_bytes(op, len(shape) if shape else 0, None, int(H))
-    if n == 0:
-        raise EccError(_lib.ECC_E_NTHRESH, f"no workspace size for op={op} H={H}")
-    return int(n)
+    key = (op, len(shape) if shape else 0, int(H))
+    n = _WS_BYTES.get(key)
+    if n is None:
+        n = int(lib.ecc_workspace_bytes(op, key[1], None, key[2]))
+        if n == 0:
+            raise EccError(_lib.ECC_E_NTHRESH, f"no workspace size for op={op} H={H}")
+        _WS_BYTES[key] = n
+    return n
 
 
 def workspace_bytes_batched(op, batch, H):
@@ -44,13 +49,32 @@ def get_workspace(nbytes, device, stream):
     key = (device.index, int(stream.cuda_stream))
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
-        with torch.cuda.stream(stream):
+        if isinstance(stream, torch.cuda.Stream):
+            with torch.cuda.stream(stream):
+                ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        else:  # the caller's current stream, which is where torch allocates
             ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
         _WS[key] = ws
     return ws
 
 
+class _CurrentStream:
+    """The caller's current stream as its raw handle (``.cuda_stream``)."""
+
+    __slots__ = ("cuda_stream",)
+
+    def __init__(self, handle):
+        self.cuda_stream = handle
+
+
+# torch's raw current-stream query costs ~0.1 us against ~2 us for building a
+# Stream object, which dominates the host time of a call on a small grid
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t):
+    if _raw_current_stream is not None:
+        return _CurrentStream(_raw_current_stream(t.get_device()))
     return torch.cuda.current_stream(t.device)
 
 
@@ -77,7 +101,7 @@ def _dev_tensor(t, name, dtype=None, device=None):
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()  # an int: the argtypes (c_void_p) convert it
 
 
 def ecc_hard_2d(grid, tau, out=None, ws=None):
@@ -95,7 +119,7 @@ def ecc_hard_2d(grid, tau, out=None, ws=None):
     ws = get_workspace(nb, grid.device, s) if ws is None else ws
     check(lib.ecc_hard_2d(_ptr(grid), _grid_dtype(grid), grid.shape[0], grid.shape[1], _ptr(tau), H,
                           _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-                          ctypes.c_void_p(s.cuda_stream)), "ecc_hard_2d")
+                          s.cuda_stream), "ecc_hard_2d")
     return out
 
 
@@ -114,7 +138,7 @@ def ecc_hard_3d(grid, tau, out=None, ws=None):
     ws = get_workspace(nb, grid.device, s) if ws is None else ws
     check(lib.ecc_hard_3d(_ptr(grid), _grid_dtype(grid), grid.shape[0], grid.shape[1], grid.shape[2],
                           _ptr(tau), H, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-                          ctypes.c_void_p(s.cuda_stream)), "ecc_hard_3d")
+                          s.cuda_stream), "ecc_hard_3d")
     return out
 
 
@@ -153,7 +177,7 @@ def ecc_hard_batched(grids, tau, out=None, ws=None):
     nb = workspace_bytes_batched(_lib.ECC_OP_HARD, B, H)
     ws = get_workspace(nb, grids.device, s) if ws is None else ws
     args = (_ptr(tau), tau_stride, H, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-            ctypes.c_void_p(s.cuda_stream))
+            s.cuda_stream)
     if grids.dim() == 3:
         check(lib.ecc_hard_2d_batched(_ptr(grids), _grid_dtype(grids), B, grids.shape[1], grids.shape[2], *args),
               "ecc_hard_2d_batched")
@@ -183,7 +207,7 @@ def ecc_soft_fwd(grid, tau, lam, out=None, ws=None):
     ws = get_workspace(nb, grid.device, s) if ws is None else ws
     check(lib.ecc_soft_fwd(_ptr(grid), grid.dim(), ctypes.cast(shp, ctypes.c_void_p), _ptr(tau), H,
                            float(lam), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-                           ctypes.c_void_p(s.cuda_stream)), "ecc_soft_fwd")
+                           s.cuda_stream), "ecc_soft_fwd")
     return out
 
 
@@ -204,7 +228,7 @@ def ecc_soft_bwd_tau(grid, tau, lam, grad_out, grad_tau=None, ws=None):
     ws = get_workspace(nb, grid.device, s) if ws is None else ws
     check(lib.ecc_soft_bwd_tau(_ptr(grid), grid.dim(), ctypes.cast(shp, ctypes.c_void_p), _ptr(tau), H,
                                float(lam), _ptr(grad_out), _ptr(grad_tau), _ptr(ws),
-                               ws.numel() * ws.element_size(), ctypes.c_void_p(s.cuda_stream)),
+                               ws.numel() * ws.element_size(), s.cuda_stream),
           "ecc_soft_bwd_tau")
     return grad_tau
 
@@ -225,7 +249,7 @@ def ecc_soft_bwd_grid(grid, tau, lam, grad_out, grad_grid=None):
     shp = _shape_arr(grid)
     s = _stream(grid)
     check(lib.ecc_soft_bwd_grid(_ptr(grid), grid.dim(), ctypes.cast(shp, ctypes.c_void_p), _ptr(tau), H,
-                                float(lam), _ptr(grad_out), _ptr(grad_grid), ctypes.c_void_p(s.cuda_stream)),
+                                float(lam), _ptr(grad_out), _ptr(grad_grid), s.cuda_stream),
           "ecc_soft_bwd_grid")
     return grad_grid
 
@@ -285,7 +309,7 @@ def ecc_soft_fwd_batched(grids, tau, lam, out=None, ws=None):
     ws = get_workspace(nb, grids.device, s) if ws is None else ws
     check(lib.ecc_soft_fwd_batched(_ptr(grids), grids.dim() - 1, ctypes.cast(shp, ctypes.c_void_p), B,
                                    _ptr(tau), ts, H, float(lam), _ptr(out), _ptr(ws),
-                                   ws.numel() * ws.element_size(), ctypes.c_void_p(s.cuda_stream)),
+                                   ws.numel() * ws.element_size(), s.cuda_stream),
           "ecc_soft_fwd_batched")
     return out
 
@@ -306,7 +330,7 @@ def ecc_soft_bwd_tau_batched(grids, tau, lam, grad_out, grad_tau=None, ws=None):
     ws = get_workspace(nb, grids.device, s) if ws is None else ws
     check(lib.ecc_soft_bwd_tau_batched(_ptr(grids), grids.dim() - 1, ctypes.cast(shp, ctypes.c_void_p), B,
                                        _ptr(tau), ts, H, float(lam), _ptr(grad_out), _ptr(grad_tau), _ptr(ws),
-                                       ws.numel() * ws.element_size(), ctypes.c_void_p(s.cuda_stream)),
+                                       ws.numel() * ws.element_size(), s.cuda_stream),
           "ecc_soft_bwd_tau_batched")
     return grad_tau
 
@@ -325,7 +349,7 @@ def ecc_soft_bwd_grid_batched(grids, tau, lam, grad_out, grad_grid=None):
     s = _stream(grids)
     check(lib.ecc_soft_bwd_grid_batched(_ptr(grids), grids.dim() - 1, ctypes.cast(shp, ctypes.c_void_p), B,
                                         _ptr(tau), ts, H, float(lam), _ptr(grad_out), _ptr(grad_grid),
-                                        ctypes.c_void_p(s.cuda_stream)),
+                                        s.cuda_stream),
           "ecc_soft_bwd_grid_batched")
     return grad_grid
 
@@ -385,7 +409,7 @@ def ecc_height(grid, dirs, alpha, out=None):
         raise ValueError("out must be [D, *grid.shape]")
     s = _stream(grid)
     check(lib.ecc_height(_ptr(grid), grid.dim(), ctypes.cast(shp, ctypes.c_void_p), _ptr(dirs), _ptr(alpha), D,
-                         _ptr(out), ctypes.c_void_p(s.cuda_stream)), "ecc_height")
+                         _ptr(out), s.cuda_stream), "ecc_height")
     return out
 
 
@@ -411,7 +435,7 @@ def ecc_height_bwd(grad_h, dirs, alpha, need_grid=True, need_dirs=True):
     check(lib.ecc_height_bwd(_ptr(grad_h), nd, ctypes.cast(shp, ctypes.c_void_p), _ptr(dirs), _ptr(alpha), D,
                              _ptr(gg) if gg is not None else null, _ptr(gd) if gd is not None else null,
                              _ptr(ga) if ga is not None else null, _ptr(ws), ws.numel() * ws.element_size(),
-                             ctypes.c_void_p(s.cuda_stream)), "ecc_height_bwd")
+                             s.cuda_stream), "ecc_height_bwd")
     return gg, gd, ga
 
 
