@@ -1148,12 +1148,19 @@ int resident_blocks(const void* kernel, int nt, size_t lds) {
   return n;
 }
 
-// Workgroups worth launching for a grid of nvox voxels and nbins bins: every
-// workgroup flushes up to nbins+1 device-scope atomics, so on small grids with
-// many bins fewer, fuller workgroups finish sooner (at least one per CU).
-int64_t useful_blocks(int64_t nvox, int nbins, int cus) {
-  const int64_t v = nvox / (4 * (int64_t)(nbins + 1));
-  return v > cus ? v : cus;
+// Workgroups worth launching for a grid of nvox voxels of esz bytes and nbins
+// bins.  Every workgroup flushes up to nbins+1 device-scope atomics, so on
+// small grids with many bins fewer, fuller workgroups finish sooner (at least
+// one per CU); and every workgroup pays its setup and flush whatever it
+// sweeps, so each should get at least 16 KiB of the grid (at least 32
+// workgroups).  Measured on 1024^2 float32 with H = 256: 20 -> 12.5 us; on
+// 2048^2 uint8: 18 -> 13 us; large grids are not capped.
+int64_t useful_blocks(int64_t nvox, int64_t esz, int nbins, int cus) {
+  int64_t v = nvox / (4 * (int64_t)(nbins + 1));
+  if (v < cus) v = cus;
+  int64_t by_bytes = nvox * esz / (16 * 1024);
+  if (by_bytes < 32) by_bytes = 32;
+  return v < by_bytes ? v : by_bytes;
 }
 
 // Threads per workgroup of the 3D float kernel.
@@ -1215,7 +1222,7 @@ hipError_t launch2d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   // short of workgroups (the per-wave row walk is serial)
   int64_t want = per_grid_blocks((int64_t)di.cus * 4, a.batch);
   {
-    const int64_t u = useful_blocks(a.ny * a.nx, nbins, di.cus);
+    const int64_t u = useful_blocks(a.ny * a.nx, DT == 0 ? 1 : 4, nbins, di.cus);
     if (want > u) want = u;
   }
   int64_t th = (a.ny * ntx) / (want * kWavesPerBlock);
@@ -1251,7 +1258,7 @@ hipError_t launch3d(const HardArgs& a, int nbins, hipStream_t s, const DeviceInf
   // split z so that there are enough tiles to fill the chip
   int64_t want = per_grid_blocks((int64_t)di.cus * (4 * 256 / NT), a.batch);
   {
-    const int64_t u = useful_blocks(a.nz * a.ny * a.nx, nbins, di.cus);
+    const int64_t u = useful_blocks(a.nz * a.ny * a.nx, DT == 0 ? 1 : 4, nbins, di.cus);
     if (want > u) want = u;
   }
   int64_t ntz = (want + ntx * nty4 - 1) / (ntx * nty4);
