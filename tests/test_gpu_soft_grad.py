@@ -2,9 +2,9 @@
 
 The HIP kernel (through the C ABI) against the float64 oracle, voxel by voxel:
 within 1e-4 relative where |value| >= 10, else 1e-3 absolute (the soft ECC
-tolerance).  At the 256^3 soft workload the oracle evaluates sampled voxels
-one by one, and the whole result is checked against the sum rule
-sum_p dL/dX(p) = -sum_k dL/dtau_k.  Every case names itself before its GPU step.
+tolerance).  At the 256^3 soft workload the oracle runs on z-slabs in worker
+processes and every voxel is compared; the whole result is also checked
+against the sum rule sum_p dL/dX(p) = -sum_k dL/dtau_k.  Every case names itself before its GPU step.
 """
 
 import zlib
@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from euler_characteristic_curves_amd import workloads as W
+from tests import slabs
 from tests.gpu_util import banner, need_gpu, soft_close
 
 pytestmark = pytest.mark.gpu
@@ -142,24 +143,18 @@ def test_soft_grad_sum_rule_and_repeat(E):
 
 @pytest.mark.timeout(600)
 def test_config_256cube_soft_grad(E):
-    """The 256^3 soft workload: sampled voxels against the per-voxel oracle
-    (faces, edges, corners and random interior voxels), plus the sum rule."""
+    """The 256^3 soft workload: every voxel against the whole-grid oracle,
+    which runs on z-slabs in spawned CPU worker processes (tests/slabs.py),
+    plus the sum rule against the GPU's own dL/dtau."""
     import torch
     g, tau, extra = W.make_workload("c5_256cube_soft")
     lam, gout = extra["lam"], extra["grad_out"]
     banner("soft grad c5")
     got = _grad_gpu(E, g, tau, lam, gout)
-    n = g.shape
-    rng = np.random.default_rng(44)
-    pts = [tuple(int(v) for v in rng.integers(0, n)) for _ in range(300)]
-    for z in (0, n[0] - 1):
-        for y in (0, 1, n[1] - 1):
-            for x in (0, 1, 63, 64, n[2] - 1):
-                pts.append((z, y, x))
-    want = oracle.ecc_soft_bwd_grid_at(g, pts, tau, lam, gout)
-    vals = np.array([got[p] for p in pts])
-    bad, worst = soft_close(vals, want)
-    assert bad.size == 0, ([pts[i] for i in bad[:5]], vals[bad[:5]], want[bad[:5]], worst)
+    banner("soft grad c5: oracle on z-slabs in worker processes")
+    want = slabs.workload_grad("c5_256cube_soft")
+    bad, worst = soft_close(got.ravel(), want.ravel())
+    assert bad.size == 0, (np.unravel_index(bad[:5], g.shape), got.ravel()[bad[:5]], want.ravel()[bad[:5]], worst)
     gt = E.ecc_soft_bwd_tau(_dev(g), _dev(tau), lam, _dev(gout))
     torch.cuda.synchronize()
     gt = gt.cpu().numpy().astype(np.float64)

@@ -235,3 +235,88 @@ def test_height_bwd_without_alpha_is_caught(monkeypatch):
     from tests import test_oracle_pins as P
     with pytest.raises(AssertionError):
         P.test_height_gradient_finite_differences((4, 5))
+
+
+# --------------------------------------- checkers of several thresholds
+# The checkers of sampled outputs on large grids, each rewritten with one
+# planted mistake; the pins in test_oracle_pins.py must reject every one.
+def _at_many_mutant(kind):
+    def f(grid, ts, slab=32):
+        grid = oecc._check_grid(grid)
+        t = np.asarray(ts, dtype=np.float32).astype(np.float64).ravel()
+        chi = np.zeros(t.size, dtype=np.int64)
+        for sub, keep in oecc._z_slabs(grid, slab):
+            if kind == "halo_twice":
+                keep = None
+            for val, dim in oecc._slab_cells(sub, keep):
+                v = val.astype(np.float64)
+                for i, ti in enumerate(t):
+                    n = np.count_nonzero(v < ti) if kind == "strict" else np.count_nonzero(v <= ti)
+                    sign = 1 if (kind == "no_sign" and dim == 1) else (-1) ** dim
+                    chi[i] += sign * int(n)
+        return chi
+    return f
+
+
+def _soft_many_mutant(kind, bwd):
+    def f(grid, ts, lam, *rest, slab=32):
+        t = np.asarray(ts, dtype=np.float32).astype(np.float64).ravel()
+        lam = oecc._check_lambda(lam)
+        acc = np.zeros(t.size, dtype=np.float64)
+        for sub, keep in oecc._z_slabs(oecc._check_grid(grid), slab):
+            if kind == "halo_twice":
+                keep = None
+            for val, dim in oecc._slab_cells(sub, keep):
+                v = val.astype(np.float64)
+                sign = 1 if kind == "no_sign" else (-1) ** dim
+                for i, ti in enumerate(t):
+                    x = (ti - v) if kind == "no_lambda_inside" else lam * (ti - v)
+                    acc[i] += sign * float((oecc._dsig(x) if bwd else oecc.sigmoid(x)).sum())
+        if not bwd:
+            return acc
+        g = np.asarray(rest[0], dtype=np.float32).astype(np.float64).ravel()
+        if kind == "g_reversed":
+            g = g[::-1]
+        scale = 1.0 if kind == "no_lambda" else lam
+        return g * scale * acc
+    return f
+
+
+@pytest.mark.parametrize("kind", ["strict", "halo_twice", "no_sign"])
+def test_at_many_mutants_are_caught(monkeypatch, kind):
+    from tests import test_oracle_pins as P
+    monkeypatch.setattr(oracle, "ecc_at_many", _at_many_mutant(kind))
+    with pytest.raises(AssertionError):
+        P.check_at_many()
+
+
+@pytest.mark.parametrize("kind", ["no_sign", "halo_twice", "no_lambda_inside"])
+def test_soft_at_many_mutants_are_caught(monkeypatch, kind):
+    from tests import test_oracle_pins as P
+    monkeypatch.setattr(oracle, "ecc_soft_at_many", _soft_many_mutant(kind, bwd=False))
+    with pytest.raises(AssertionError):
+        P.check_soft_at_many()
+
+
+@pytest.mark.parametrize("kind", ["no_sign", "halo_twice", "no_lambda", "no_lambda_inside", "g_reversed"])
+def test_soft_bwd_at_many_mutants_are_caught(monkeypatch, kind):
+    from tests import test_oracle_pins as P
+    monkeypatch.setattr(oracle, "ecc_soft_bwd_at_many", _soft_many_mutant(kind, bwd=True))
+    with pytest.raises(AssertionError):
+        P.check_soft_bwd_at_many()
+
+
+@pytest.mark.parametrize("name", ["ecc_at_many", "ecc_soft_at_many", "ecc_soft_bwd_at_many"])
+def test_many_mutant_builders_reproduce_the_oracle_unplanted(monkeypatch, name):
+    """The rewrites above, with nothing planted, pass the same pins, so each
+    mutant fails only because of its planted mistake."""
+    from tests import test_oracle_pins as P
+    if name == "ecc_at_many":
+        monkeypatch.setattr(oracle, name, _at_many_mutant("none"))
+        P.check_at_many()
+    elif name == "ecc_soft_at_many":
+        monkeypatch.setattr(oracle, name, _soft_many_mutant("none", bwd=False))
+        P.check_soft_at_many()
+    else:
+        monkeypatch.setattr(oracle, name, _soft_many_mutant("none", bwd=True))
+        P.check_soft_bwd_at_many()

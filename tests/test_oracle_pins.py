@@ -505,3 +505,66 @@ def test_height_gradient_finite_differences(shape):
         dn[p] -= h
         fd = (loss(up, U, A) - loss(dn, U, A)) / (2 * h)
         assert abs(fd - dX[p]) < 1e-5 * max(1.0, abs(fd)), ("X", p, fd, dX[p])
+
+
+# ------------------------------------------- several thresholds in one pass
+# ecc_at_many, ecc_soft_at_many and ecc_soft_bwd_at_many check sampled outputs
+# of large grids.  Each is pinned here to the cell-by-cell counts and sums of
+# tests/pins.py on tiny grids: thresholds equal to cell values (the inclusive
+# compare), duplicated and unsorted thresholds, per-threshold upstream
+# gradients (the index that pairs g_k with tau_k), and z-slabs of one or two
+# planes (the halo plane of each slab is counted once).
+
+def _many_cases(seed):
+    rng = np.random.default_rng(seed)
+    for ndim, count in ((2, 8), (3, 6)):
+        for i in range(count):
+            if i % 2:
+                g = _rand_small(rng, ndim, hi=4, max_side=6 if ndim == 2 else 4)
+            else:
+                shape = tuple(int(s) for s in rng.integers(1, 6 if ndim == 2 else 5, size=ndim))
+                g = rng.random(shape).astype(np.float32)
+            vals = np.unique(g)
+            ts = np.concatenate([vals[rng.integers(0, vals.size, 3)], [vals[0] - 0.25, vals[-1]],
+                                 vals[:1], rng.uniform(-0.5, 4.5, 2)]).astype(np.float32)
+            yield g, rng.permutation(ts)
+
+
+def check_at_many():
+    for g, ts in _many_cases(501):
+        want = [pins.brute_chi(g, float(t)) for t in ts]
+        for slab in (None, 1, 2):
+            got = oracle.ecc_at_many(g, ts, slab=slab)
+            assert got.dtype == np.int64 and got.tolist() == want, (g.shape, slab, got.tolist(), want)
+
+
+def check_soft_at_many():
+    for lam in (3.0, 40.0):
+        for g, ts in _many_cases(502):
+            want = pins.soft_by_hand(g, ts, lam)
+            for slab in (None, 1, 2):
+                got = oracle.ecc_soft_at_many(g, ts, lam, slab=slab)
+                np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def check_soft_bwd_at_many():
+    rng = np.random.default_rng(503)
+    for lam in (3.0, 40.0):
+        for g, ts in _many_cases(504):
+            gs = rng.standard_normal(ts.size).astype(np.float32)
+            want = pins.soft_bwd_by_hand(g, ts, lam, gs)
+            for slab in (None, 1, 2):
+                got = oracle.ecc_soft_bwd_at_many(g, ts, lam, gs, slab=slab)
+                np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
+
+
+def test_ecc_at_many_matches_brute_force():
+    check_at_many()
+
+
+def test_soft_at_many_matches_by_hand():
+    check_soft_at_many()
+
+
+def test_soft_bwd_at_many_matches_by_hand():
+    check_soft_bwd_at_many()
