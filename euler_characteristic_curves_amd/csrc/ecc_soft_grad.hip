@@ -25,8 +25,21 @@
 // the middle of the threshold range), s(1 - s) = t / (1 + t)^2, so
 //     h(v) = F sum_k (g_k E_k) r_k^2,  r_k = 1 / (1 + F E_k),
 // one FMA, one reciprocal, one multiply and one FMA per (voxel, threshold).
-// Where the factors would leave the float range (very wide threshold span or
-// huge upstream gradients) every pair takes exp2 directly.
+// Where the factors would leave the float range (a threshold span much wider
+// than 1 / lambda) every pair takes exp2 directly.
+//
+// Accuracy.  Terms are float32, summed in float32 over 8 thresholds and in
+// float64 beyond.  The table holds the thresholds with g_k > 0 first and
+// those with g_k < 0 after (g_k = 0 adds nothing and is left out), so the two
+// partial sums give both h and m = sum_k |g_k| s(1 - s), the scale of the
+// rounding error: every term is within a few float32 units of itself, so the
+// error of h is below K u m (u = 2^-24; K derived at kFactoredK / kDirectK).
+// Where h cancels (upstream gradients of both signs that are large, or a
+// large lambda |c(p)|) that bound can exceed the accuracy the soft outputs
+// are held to; such voxels are recomputed term by term in float64 from the
+// defining formula, so every output is within kAbsTarget or kRelTarget of
+// the exact value.  Upstream gradients enter the table scaled by a power of
+// two, which is exact and keeps g_k E_k inside the float range.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -43,6 +56,31 @@ constexpr int kGradWaves = kGradNT / 64;
 constexpr int kSlots = 4;                  // queued voxels per lane in one sweep
 constexpr int kBatch = 64 * kSlots;        // voxels per sweep
 constexpr int kQueueCap = kBatch + 64;     // a sweep starts once >= kBatch are queued
+constexpr int kBlk = 8;                    // thresholds per float32 partial sum
+constexpr int kTablePad = 2 * kBlk;        // table entries beyond H (segment padding)
+
+// Every output is within max(kAbsTarget, kRelTarget |exact|) of the exact
+// value: 90 % of the soft tolerance (1e-3 absolute, 1e-4 relative), leaving
+// the rest for the final rounding to float (below 6e-8 relative).
+constexpr double kAbsTarget = 9e-4;
+constexpr double kRelTarget = 9e-5;
+constexpr double kU = 0x1p-24;  // float32 unit roundoff
+// Factored terms gs E r r (r = 1 / (1 + F E), F applied in float64 after the
+// sum).  E and F are float64 exp2 values rounded to float (u each); gs E and
+// (gs E) r are rounded once each (u, u); 1 + F E is one FMA (u) and r one
+// reciprocal (2 u).  With t = F E, a relative error e in F or E moves
+// E r^2 F by e (1 - t) / (1 + t), at most e, so a term is within
+// u + u + u + u + 2 (u + 2 u) = 10 u of itself; the float32 sum of 8
+// same-signed terms adds 8 u of their sum: 18 u, taken as 20.
+constexpr double kFactoredK = 20.0 * kU;
+constexpr int kRefCap = 64;   // per-wave list of voxels for the float64 path
+// Direct terms: the exponent x = L (v - tau) is three float32 roundings away
+// from exact (3 u |x| in log2 units, 2.08 u |x| relative after exp2), then
+// exp2 (2 u), 1 + t, the reciprocal and three multiplies: 2.08 u |x| + 11 u
+// per term, + 8 u for the partial sums.  The bound K u m + Kx u sum |term| |x|
+// with K = 24, Kx = 4.
+constexpr double kDirectK = 24.0 * kU;
+constexpr double kDirectKx = 4.0 * kU;
 
 struct QEntry {
   float v;        // X(p)
@@ -51,13 +89,35 @@ struct QEntry {
 };
 
 struct GradCtx {
-  const float2* T;  // per threshold: (E_k, g_k E_k) factored, (tau_k, g_k) direct
-  int Hp;           // table length, H rounded up to even (pad entries are (0, 0))
+  // per threshold: (E_k, gs_k E_k) factored, (tau_k, gs_k) direct, gs = g / 2^s;
+  // [0, nP): g > 0, [nP, nP + nN): g < 0, each padded with (0, 0) to kBlk
+  const float2* T;
+  int nP, nN;
   bool factored;
   double L64, cen;
-  float Lf, lambda;
+  float Lf;
+  double lam64;
+  double gscale;  // 2^s
+  double ginv;    // factored: sum_k |gs_k| / E_k
+  double g1;      // sum_k |gs_k|
+  const float* tau;   // the raw thresholds and upstream gradient (float64 path)
+  const float* gout;
+  int H;
   float* out;
 };
+
+// Wave-uniform copies (values read from LDS are uniform but would otherwise
+// stay in vector registers for the whole kernel).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uni(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+__device__ __forceinline__ double uni(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_readfirstlane((int)(b & 0xffffffffLL));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
 
 // Orders this wave's LDS accesses around it (queue writes by some lanes are
 // read by other lanes of the same wave).
@@ -67,56 +127,147 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Phase B: sum h over all thresholds for queue entries q[0..n) (n <= kBatch),
-// lane l taking entries l, l + 64, l + 128, l + 192; write the gradients.
-__device__ __forceinline__ void sweep(const GradCtx& g, const QEntry* q, int n, int lane) {
-  float a[kSlots];
-  float wc[kSlots];
-  long long id[kSlots];
+// Table entries [k0, k1) (float4 units, 2 thresholds each, k1 - k0 a multiple
+// of kBlk / 2), factored form: acc[j] += F-free sum of gs E r^2.
+__device__ __forceinline__ void seg_factored(const float4* T4, int k0, int k1, const float* a, double* acc) {
+  for (int k = k0; k < k1; k += kBlk / 2) {
+    float blk[kSlots] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    const int e = lane + 64 * j;
-    const bool ok = e < n;
-    const QEntry qe = q[ok ? e : 0];
-    id[j] = ok ? qe.idx : -1;
-    wc[j] = (float)qe.c;
-    // F kept finite, so F E overflowing to inf only ever meets a 0 reciprocal
-    a[j] = g.factored ? fminf(exp2_split(g.L64 * ((double)qe.v - g.cen)), 0x1p126f) : qe.v;
-  }
-  float acc[kSlots] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const float4* T4 = reinterpret_cast<const float4*>(g.T);
-  const int n2 = g.Hp >> 1;
-  if (g.factored) {
-    for (int k = 0; k < n2; ++k) {
-      const float4 t = T4[k];
+    for (int u = 0; u < kBlk / 2; ++u) {
+      const float4 t = T4[k + u];
 #pragma unroll
       for (int j = 0; j < kSlots; ++j) {
         const float r0 = __builtin_amdgcn_rcpf(fmaf(a[j], t.x, 1.0f));
-        acc[j] = fmaf(t.y * r0, r0, acc[j]);
+        blk[j] = fmaf(t.y * r0, r0, blk[j]);
         const float r1 = __builtin_amdgcn_rcpf(fmaf(a[j], t.z, 1.0f));
-        acc[j] = fmaf(t.w * r1, r1, acc[j]);
+        blk[j] = fmaf(t.w * r1, r1, blk[j]);
       }
     }
-  } else {
-    for (int k = 0; k < n2; ++k) {
-      const float4 t = T4[k];
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) acc[j] += (double)blk[j];
+  }
+}
+
+// The same with exp2 per pair (a = v); mw[j] += |term| |x|, x the exponent.
+__device__ __forceinline__ void seg_direct(const float4* T4, int k0, int k1, float Lf, const float* a,
+                                           double* acc, float* mw) {
+  for (int k = k0; k < k1; k += kBlk / 2) {
+    float blk[kSlots] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < kBlk / 2; ++u) {
+      const float4 t = T4[k + u];
 #pragma unroll
       for (int j = 0; j < kSlots; ++j) {
-        const float t0 = __builtin_amdgcn_exp2f(fminf(g.Lf * (a[j] - t.x), 126.0f));
-        const float r0 = __builtin_amdgcn_rcpf(1.0f + t0);
-        acc[j] = fmaf(t.y * (t0 * r0), r0, acc[j]);
-        const float t1 = __builtin_amdgcn_exp2f(fminf(g.Lf * (a[j] - t.z), 126.0f));
-        const float r1 = __builtin_amdgcn_rcpf(1.0f + t1);
-        acc[j] = fmaf(t.w * (t1 * r1), r1, acc[j]);
+        const float x0 = fmaxf(fminf(Lf * (a[j] - t.x), 126.0f), -150.0f);
+        const float e0 = __builtin_amdgcn_exp2f(x0);
+        const float r0 = __builtin_amdgcn_rcpf(1.0f + e0);
+        const float s0 = (t.y * (e0 * r0)) * r0;
+        blk[j] += s0;
+        mw[j] = fmaf(fabsf(s0), fabsf(x0), mw[j]);
+        const float x1 = fmaxf(fminf(Lf * (a[j] - t.z), 126.0f), -150.0f);
+        const float e1 = __builtin_amdgcn_exp2f(x1);
+        const float r1 = __builtin_amdgcn_rcpf(1.0f + e1);
+        const float s1 = (t.w * (e1 * r1)) * r1;
+        blk[j] += s1;
+        mw[j] = fmaf(fabsf(s1), fabsf(x1), mw[j]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) acc[j] += (double)blk[j];
   }
+}
+
+// h(v) term by term in float64, sum_k g_k e / (1 + e)^2 with
+// e = exp(-|lambda (tau_k - v)|), for the m (wave-uniform) voxels listed in
+// R: the wave takes one voxel at a time, lane l summing thresholds l, l + 64,
+// ..., then a fixed-order butterfly (lane 0's total is written, so the
+// result does not depend on scheduling).
+__device__ __forceinline__ void refine_list(const GradCtx& g, const QEntry* R, int m, int lane) {
+  for (int i = 0; i < m; ++i) {
+    const QEntry e = R[i];
+    const double vd = e.v;
+    double h = 0.0;
+    for (int k = lane; k < g.H; k += 64) {
+      const double x = exp(-fabs(g.lam64 * ((double)g.tau[k] - vd)));
+      const double r = 1.0 / (1.0 + x);
+      h += (double)g.gout[k] * (x * r * r);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) h += __shfl_xor(h, off);
+    if (lane == 0) g.out[e.idx] = (float)(-g.lam64 * (double)e.c * h);
+  }
+}
+
+// Phase B: sum h over all thresholds for queue entries q[0..n) (n <= kBatch),
+// lane l taking entries l, l + 64, l + 128, l + 192; write the gradients, or
+// list the voxel in R for the float64 path (done before the next slot).
+__device__ __forceinline__ void sweep(const GradCtx& g, const QEntry* q, int n, int lane, QEntry* R) {
+  int rcount = 0;  // wave-uniform
+  float a[kSlots];
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) {
-    if (id[j] < 0) continue;
-    double h = (double)acc[j];
-    if (g.factored) h *= (double)a[j];
-    g.out[id[j]] = (float)(-(double)g.lambda * (double)wc[j] * h);
+    const int e = lane + 64 * j;
+    const float v = q[e < n ? e : 0].v;
+    // F rounded from float64 and kept finite, so F E overflowing to inf only
+    // ever meets a 0 reciprocal (voxels with F > 2^126 are handled apart)
+    a[j] = g.factored ? (float)fmin(exp2(g.L64 * ((double)v - g.cen)), 0x1p126) : v;
+  }
+  double accP[kSlots] = {0.0, 0.0, 0.0, 0.0};
+  double accN[kSlots] = {0.0, 0.0, 0.0, 0.0};
+  float mw[kSlots] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float4* T4 = reinterpret_cast<const float4*>(g.T);
+  const int eP = g.nP >> 1, eN = (g.nP + g.nN) >> 1;
+  if (g.factored) {
+    seg_factored(T4, 0, eP, a, accP);
+    seg_factored(T4, eP, eN, a, accN);
+  } else {
+    seg_direct(T4, 0, eP, g.Lf, a, accP, mw);
+    seg_direct(T4, eP, eN, g.Lf, a, accN, mw);
+  }
+  // the queue entries are still in place: reload them rather than hold them
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    const int e = lane + 64 * j;
+    bool need = false;
+    QEntry qe;
+    if (e < n) {
+      qe = q[e];
+      const double lc = g.lam64 * fabs((double)qe.c);  // lambda |c(p)|
+      double h, err;
+      if (g.factored) {
+        const double aF = g.L64 * ((double)qe.v - g.cen);
+        if (aF > 126.0) {
+          // above every threshold by more than 26 / L (F was clamped): s(1 - s)
+          // <= 1 / t, so |h| <= 2^-aF sum_k |g_k| / E_k; take h = 0 with that error
+          h = 0.0;
+          err = exp2(-aF) * g.ginv * g.gscale;
+        } else {
+          // the float F of the sum, or float64 below the normal float range
+          const double sc = (aF >= -126.0 ? (double)a[j] : exp2(aF)) * g.gscale;
+          h = (accP[j] + accN[j]) * sc;
+          // + underflow of g E below the float range: under 2^-147 per entry
+          err = (kFactoredK * (accP[j] - accN[j]) + (double)(g.nP + g.nN) * 0x1p-147) * sc;
+        }
+      } else {
+        h = (accP[j] + accN[j]) * g.gscale;
+        // + the exponent clamps and underflow: under 2^-50 of sum |gs_k|
+        err = (kDirectK * (accP[j] - accN[j]) + kDirectKx * (double)mw[j] + g.g1 * 0x1p-50) * g.gscale;
+      }
+      need = lc * err > fmax(kAbsTarget, kRelTarget * lc * fmax(fabs(h) - err, 0.0));
+      if (!need) g.out[qe.idx] = (float)(-g.lam64 * (double)qe.c * h);
+    }
+    const uint64_t bal = __ballot(need);
+    if (need) {
+      R[rcount + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u))] = qe;
+    }
+    rcount += __popcll(bal);
+    if (rcount > 0) {
+      wave_lds_sync();
+      refine_list(g, R, rcount, lane);
+      rcount = 0;
+      wave_lds_sync();
+    }
   }
 }
 
@@ -143,68 +294,149 @@ __global__ __launch_bounds__(kGradNT) void soft_grad_kernel(GradArgs p, int64_t 
     p.grad_out += b * p.H;
   }
   QEntry* queues = reinterpret_cast<QEntry*>(smem);                     // kGradWaves x kQueueCap
-  float2* T = reinterpret_cast<float2*>(queues + kGradWaves * kQueueCap);
-  float* red = reinterpret_cast<float*>(smem);                          // setup only, 3 x kGradNT
+  QEntry* rlists = queues + kGradWaves * kQueueCap;                     // kGradWaves x kRefCap
+  float2* T = reinterpret_cast<float2*>(rlists + kGradWaves * kRefCap);  // H + kTablePad entries
+  // set-up scratch, overlaying the queues: 3 x kGradNT floats + 2 x kGradNT
+  // ints, then 2 x kGradWaves ints (table order), then 2 x kGradNT doubles
+  float* red = reinterpret_cast<float*>(smem);
+  int* redi = reinterpret_cast<int*>(red + 3 * kGradNT);
+  int* cnt = reinterpret_cast<int*>(smem);
+  double* redd = reinterpret_cast<double*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = p.H, Hp = (H + 1) & ~1;
+  const int H = p.H;
   const float INF = __builtin_inff();
 
-  // ---------------- threshold range, largest |g|: factored form or not
+  // ---------------- threshold range, largest |g|, how many g > 0 and g < 0
   {
     float lo = INF, hi = -INF, gm = 0.0f;
+    int np = 0, nn = 0;
     for (int k = tid; k < H; k += kGradNT) {
-      const float t = p.tau[k];
+      const float t = p.tau[k], gk = p.grad_out[k];
       lo = fminf(lo, t);
       hi = fmaxf(hi, t);
-      gm = fmaxf(gm, fabsf(p.grad_out[k]));
+      gm = fmaxf(gm, fabsf(gk));
+      np += gk > 0.0f;
+      nn += gk < 0.0f;
     }
     red[tid] = lo;
     red[kGradNT + tid] = hi;
     red[2 * kGradNT + tid] = gm;
+    redi[tid] = np;
+    redi[kGradNT + tid] = nn;
     __syncthreads();
     for (int off = kGradNT / 2; off > 0; off >>= 1) {
       if (tid < off) {
         red[tid] = fminf(red[tid], red[tid + off]);
         red[kGradNT + tid] = fmaxf(red[kGradNT + tid], red[kGradNT + tid + off]);
         red[2 * kGradNT + tid] = fmaxf(red[2 * kGradNT + tid], red[2 * kGradNT + tid + off]);
+        redi[tid] += redi[tid + off];
+        redi[kGradNT + tid] += redi[kGradNT + tid + off];
       }
       __syncthreads();
     }
   }
-  const float tlo = red[0], thi = red[kGradNT], gmax = red[2 * kGradNT];
+  const float tlo = uni(red[0]), thi = uni(red[kGradNT]), gmax = uni(red[2 * kGradNT]);
+  const int P = uni(redi[0]), N = uni(redi[kGradNT]);
+  __syncthreads();  // the scratch is reused below
+
   GradCtx g;
   g.L64 = (double)p.lambda * 1.4426950408889634074;  // lambda * log2(e)
   g.cen = 0.5 * ((double)tlo + (double)thi);
   const double half_span = g.L64 * 0.5 * ((double)thi - (double)tlo);
-  // E in [2^-100, 2^100] and |g E| <= 2^124; false for inf/NaN spans or gradients
-  g.factored = (half_span >= 0.0) && (half_span <= 100.0) && (gmax <= 0x1p24f);
+  // E in [2^-100, 2^100]; false for inf/NaN spans
+  g.factored = (half_span >= 0.0) && (half_span <= 100.0);
   g.Lf = (float)g.L64;
-  g.lambda = p.lambda;
+  g.lam64 = (double)p.lambda;
   g.out = p.out;
   g.T = T;
-  g.Hp = Hp;
-  for (int k = tid; k < Hp; k += kGradNT) {
-    float2 e = make_float2(0.0f, 0.0f);
-    if (k < H) {
-      const float tk = p.tau[k], gk = p.grad_out[k];
-      if (g.factored) {
-        const float E = exp2_split(g.L64 * (g.cen - (double)tk));
-        e = make_float2(E, gk * E);
-      } else {
-        e = make_float2(tk, gk);
+  g.tau = p.tau;
+  g.gout = p.grad_out;
+  g.H = H;
+  g.nP = (P + kBlk - 1) & ~(kBlk - 1);
+  g.nN = (N + kBlk - 1) & ~(kBlk - 1);
+  // gs = g / 2^s with max |gs| in [1, 2): |gs E| <= 2^101
+  int sh = gmax > 0.0f ? ilogbf(gmax) : 0;
+  sh = sh < -200 ? -200 : (sh > 200 ? 200 : sh);
+  g.gscale = ldexp(1.0, sh);
+
+  // ---------------- the table: g > 0 in threshold order, then g < 0
+  double ginv = 0.0, g1 = 0.0;
+  {
+    int runP = 0, runN = 0;
+    for (int base = 0; base < H; base += kGradNT) {
+      const int k = base + tid;
+      float tk = 0.0f, gk = 0.0f;
+      if (k < H) {
+        tk = p.tau[k];
+        gk = p.grad_out[k];
       }
+      const bool pos = gk > 0.0f, neg = gk < 0.0f;
+      const uint64_t bp = __ballot(pos), bn = __ballot(neg);
+      if (lane == 0) {
+        cnt[wave] = __popcll(bp);
+        cnt[kGradWaves + wave] = __popcll(bn);
+      }
+      __syncthreads();
+      int offP = runP, offN = runN;
+      for (int w = 0; w < kGradWaves; ++w) {
+        const int cp = cnt[w], cn = cnt[kGradWaves + w];
+        if (w < wave) {
+          offP += cp;
+          offN += cn;
+        }
+        runP += cp;
+        runN += cn;
+      }
+      if (pos || neg) {
+        const uint64_t bal = pos ? bp : bn;
+        const int below = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+        const int slot = pos ? offP + below : g.nP + offN + below;
+        const float gs = ldexpf(gk, -sh);
+        float2 e;
+        if (g.factored) {
+          const float E = (float)exp2(g.L64 * (g.cen - (double)tk));
+          e = make_float2(E, gs * E);
+          ginv += fabs((double)gs) / (double)E;
+        } else {
+          e = make_float2(tk, gs);
+        }
+        g1 += fabs((double)gs);
+        T[slot] = e;
+      }
+      __syncthreads();  // cnt is rewritten by the next chunk
     }
-    T[k] = e;
   }
+  for (int k = P + tid; k < g.nP; k += kGradNT) T[k] = make_float2(0.0f, 0.0f);
+  for (int k = g.nP + N + tid; k < g.nP + g.nN; k += kGradNT) T[k] = make_float2(0.0f, 0.0f);
+  redd[tid] = ginv;
+  redd[kGradNT + tid] = g1;
   __syncthreads();
+  for (int off = kGradNT / 2; off > 0; off >>= 1) {
+    if (tid < off) {
+      redd[tid] += redd[tid + off];
+      redd[kGradNT + tid] += redd[kGradNT + tid + off];
+    }
+    __syncthreads();
+  }
+  g.ginv = uni(redd[0]);
+  g.g1 = uni(redd[kGradNT]);
+  // wave-uniform: scalar registers rather than vector pairs across the loop
+  g.L64 = uni(g.L64);
+  g.cen = uni(g.cen);
+  g.lam64 = uni(g.lam64);
+  g.gscale = uni(g.gscale);
+  g.Lf = uni(g.Lf);
+  __syncthreads();  // the queues overlay the scratch
 
   // ---------------- segments of 64 voxels, one per wave at a time
   const float* grid = p.grid;
   const int64_t nz = p.nz, ny = p.ny, nx = p.nx;
   const int64_t plane = ny * nx, nvox = nz * plane;
   QEntry* q = queues + wave * kQueueCap;
+  QEntry* R = rlists + wave * kRefCap;
   int count = 0;  // wave-uniform
   const int64_t wstride = (int64_t)gridDim.x * kGradWaves;
   // (z0, y0, x0) of the segment's first voxel, advanced by the grid stride
@@ -287,7 +519,7 @@ __global__ __launch_bounds__(kGradNT) void soft_grad_kernel(GradArgs p, int64_t 
     count += __popcll(bal);
     if (count >= kBatch) {
       wave_lds_sync();
-      sweep(g, q + (count - kBatch), kBatch, lane);
+      sweep(g, q + (count - kBatch), kBatch, lane, R);
       count -= kBatch;
       wave_lds_sync();
     }
@@ -305,14 +537,15 @@ __global__ __launch_bounds__(kGradNT) void soft_grad_kernel(GradArgs p, int64_t 
   }
   if (count > 0) {
     wave_lds_sync();
-    sweep(g, q, count, lane);
+    sweep(g, q, count, lane, R);
   }
 }
 
 template <bool D3>
 hipError_t launch_grad(const GradArgs& a, hipStream_t s, int64_t nseg, const DeviceInfo& di) {
   auto k = soft_grad_kernel<D3>;
-  const size_t lds = (size_t)kGradWaves * kQueueCap * sizeof(QEntry) + (size_t)((a.H + 1) & ~1) * sizeof(float2);
+  const size_t lds = (size_t)kGradWaves * (kQueueCap + kRefCap) * sizeof(QEntry) +
+                     (size_t)(a.H + kTablePad) * sizeof(float2);
   hipError_t e;
   if (lds > 64 * 1024) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
