@@ -30,7 +30,7 @@ ECC_MAX_DIRECTIONS = 4096
 EXPORTS = (
     "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
     "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
-    "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_grid_batched",
+    "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_tau_shared", "ecc_soft_bwd_grid_batched",
     "ecc_height", "ecc_height_bwd", "ecc_height_workspace_bytes",
     "ecc_workspace_bytes", "ecc_workspace_bytes_batched", "ecc_status_string", "ecc_last_error", "ecc_version",
 )
@@ -70,6 +70,8 @@ def _load():
     lib.ecc_soft_fwd_batched.restype = I
     lib.ecc_soft_bwd_tau_batched.argtypes = [P, I32, P, I64, P, I64, I32, F, P, P, P, SZ, P]
     lib.ecc_soft_bwd_tau_batched.restype = I
+    lib.ecc_soft_bwd_tau_shared.argtypes = [P, I32, P, I64, P, I32, F, P, P, P, SZ, P]
+    lib.ecc_soft_bwd_tau_shared.restype = I
     lib.ecc_soft_bwd_grid_batched.argtypes = [P, I32, P, I64, P, I64, I32, F, P, P, P]
     lib.ecc_soft_bwd_grid_batched.restype = I
     lib.ecc_height.argtypes = [P, I32, P, P, P, I32, P, P]

@@ -251,6 +251,24 @@ int ecc_soft_bwd_tau_batched(const float* grid, int32_t ndim, const int64_t* sha
   return hip_status(ecc::launch_soft(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int ecc_soft_bwd_tau_shared(const float* grid, int32_t ndim, const int64_t* shape, int64_t batch,
+                            const float* tau, int32_t H, float lambda, const float* grad_out, float* grad_tau,
+                            void* ws, size_t ws_bytes, void* stream) {
+  int64_t d[3];
+  int st = check_soft(grid, ndim, shape, tau, H, lambda, grad_tau, ws, ws_bytes, d, false);
+  if (st != ECC_OK) return st;
+  if (!grad_out) return fail(ECC_E_NULL, "%sgrad_out is NULL");
+  st = check_batch(batch, 0, d[0] * d[1] * d[2], ws, ws_bytes, H, true);
+  if (st != ECC_OK) return st;
+  ecc::SoftArgs a{grid, d[0], d[1], d[2], tau, H, lambda, grad_out, grad_tau, ws};
+  a.batch = batch;
+  a.tau_stride = 0;
+  a.ws_stride = ecc::batch_ws_stride(H, batch);
+  a.acc_copies = ecc::batch_copies(batch);
+  a.sum_batch = batch;
+  return hip_status(ecc::launch_soft(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int ecc_soft_bwd_grid_batched(const float* grid, int32_t ndim, const int64_t* shape, int64_t batch,
                               const float* tau, int64_t tau_stride, int32_t H, float lambda,
                               const float* grad_out, float* grad_grid, void* stream) {

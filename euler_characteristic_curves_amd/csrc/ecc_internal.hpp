@@ -62,7 +62,16 @@ struct SoftArgs {
   int64_t tau_stride = 0;
   size_t ws_stride = 0;
   int acc_copies = kAccCopies;
+  // Backward with thresholds shared by the batch, summed over it: out is the
+  // one float32[H] gradient of tau.  sum_batch = the whole batch (0: off),
+  // ws_base = the workspace of grid 0, b_first = this launch's first grid.
+  int64_t sum_batch = 0;
+  void* ws_base = nullptr;
+  int64_t b_first = 0;
 };
+
+// Grids per group of the two-level batch sum (soft backward, shared tau).
+constexpr int64_t kSumGroup = 64;
 
 struct GradArgs {
   const float* grid;

@@ -45,6 +45,8 @@ constexpr int kLaneGroups = 2;          // terms a wave sweeps at once
 constexpr int kGroupLanes = 64 / kLaneGroups;
 constexpr int kSlots = kChunk / kGroupLanes;  // thresholds per lane and chunk
 
+__device__ void batch_sum(const SoftArgs& p, const long long* tot, double inv, int* flag);
+
 struct Term {
   float a;  // F = 2^{L (v - c)} (factored) or the value v (direct)
   float w;  // summed sign
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles
     const int64_t b = blockIdx.y;
     p.grid += b * (p.nz * p.ny * p.nx);
     p.tau += b * p.tau_stride;
-    p.out += b * p.H;
+    if (p.sum_batch == 0) p.out += b * p.H;
     if (BWD) p.grad_out += b * p.H;
     p.ws = reinterpret_cast<char*>(p.ws) + (size_t)b * p.ws_stride;
   }
@@ -245,9 +247,18 @@ __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles
           }
         }
       }
+      // this wave's two lane groups, then the waves one after another: a
+      // fixed order of additions, so the sums do not depend on scheduling
 #pragma unroll
-      for (int r = 0; r < kSlots; ++r)
-        if (valid[r]) atomicAdd(&accS[c * kChunk + r * kGroupLanes + gl], acc[r]);
+      for (int r = 0; r < kSlots; ++r) acc[r] += __shfl_down(acc[r], kGroupLanes);
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        if (wave == w && grp == 0) {
+#pragma unroll
+          for (int r = 0; r < kSlots; ++r)
+            if (valid[r]) accS[c * kChunk + r * kGroupLanes + gl] += acc[r];
+        }
+        __syncthreads();
+      }
     }
     __syncthreads();
     if (tid == 0) misc[0] = 0;
@@ -262,10 +273,75 @@ __global__ __launch_bounds__(kBlock) void soft_kernel(SoftArgs p, int64_t ntiles
                    p.acc_copies))
     return;
   const double inv = ldexp(1.0, -fx_shift);
+  if (!BWD || p.sum_batch == 0) {
+    for (int k = tid; k < H; k += kBlock) {
+      double v = (double)tot[k] * inv;
+      if constexpr (BWD) v *= (double)p.lambda * (double)p.grad_out[k];
+      p.out[k] = (float)v;
+    }
+    return;
+  }
+  if constexpr (BWD) batch_sum(p, tot, inv, &misc[1]);
+}
+
+// The shared-threshold gradient summed over the batch, in a fixed order.
+// The last workgroup of grid b leaves its float64 values in the accumulator
+// slots of its own workspace slice (grid_reduce has just cleared them).  Grids
+// form groups of kSumGroup; the last grid of a group to finish (ticket in the
+// header of the group's first slice) sums the group's slots in grid order into
+// the group's first slot and clears the others; the last group (ticket in
+// grid 0's header) sums the group totals in order, writes out and clears
+// them, so the workspace is zero again.  Tickets and slots use device-scope
+// atomics, ordered as in grid_reduce.
+__device__ void batch_sum(const SoftArgs& p, const long long* tot, double inv, int* flag) {
+  const int tid = threadIdx.x, H = p.H;
+  const int64_t B = p.sum_batch, bg = p.b_first + blockIdx.y;
+  char* const base = reinterpret_cast<char*>(p.ws_base);
+  auto slot = [&](int64_t b) { return reinterpret_cast<double*>(base + (size_t)b * p.ws_stride + kWsHeader); };
+  auto ticket = [&](int64_t b, int i) { return reinterpret_cast<unsigned int*>(base + (size_t)b * p.ws_stride) + i; };
+  auto last_of = [&](unsigned int* t, int64_t n) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned int prev = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = prev == (unsigned int)(n - 1);
+      if (last) __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *flag = last;
+    }
+    __syncthreads();
+    return *flag != 0;
+  };
+  // in-order sum of `n` slots starting at grid b0, stride `step` grids
+  auto ordered_sum = [&](int64_t b0, int64_t n, int64_t step, int k) {
+    double s = 0.0;
+    int64_t i = 0;
+    for (; i + 8 <= n; i += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = agent_load(slot(b0 + (i + u) * step) + k);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; i < n; ++i) s += agent_load(slot(b0 + i * step) + k);
+    return s;
+  };
+  __syncthreads();
+  double* mine = slot(bg);
+  for (int k = tid; k < H; k += kBlock)
+    agent_store(mine + k, (double)tot[k] * inv * (double)p.lambda * (double)p.grad_out[k]);
+  const int64_t g0 = bg - bg % kSumGroup;
+  const int64_t ng = B - g0 < kSumGroup ? B - g0 : kSumGroup;
+  if (!last_of(ticket(g0, 1), ng)) return;
   for (int k = tid; k < H; k += kBlock) {
-    double v = (double)tot[k] * inv;
-    if constexpr (BWD) v *= (double)p.lambda * (double)p.grad_out[k];
-    p.out[k] = (float)v;
+    const double s = ordered_sum(g0, ng, 1, k);
+    agent_store(slot(g0) + k, s);
+    for (int64_t b = g0 + 1; b < g0 + ng; ++b) agent_store(slot(b) + k, 0.0);
+  }
+  const int64_t ngroups = (B + kSumGroup - 1) / kSumGroup;
+  if (!last_of(ticket(0, 2), ngroups)) return;
+  for (int k = tid; k < H; k += kBlock) {
+    p.out[k] = (float)ordered_sum(0, ngroups, kSumGroup, k);
+    for (int64_t j = 0; j < ngroups; ++j) agent_store(slot(j * kSumGroup) + k, 0.0);
   }
 }
 
@@ -306,6 +382,11 @@ hipError_t launch_soft(const SoftArgs& a, hipStream_t s) {
     c.out = a.out + b0 * a.H;
     if (a.grad_out) c.grad_out = a.grad_out + b0 * a.H;
     c.ws = reinterpret_cast<char*>(a.ws) + (size_t)b0 * a.ws_stride;
+    if (a.sum_batch) {
+      c.out = a.out;
+      c.ws_base = a.ws;
+      c.b_first = b0;
+    }
     hipLaunchKernelGGL(k, dim3((unsigned)g, (unsigned)nb), dim3(kBlock), lds, s, c, ntiles, shift);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

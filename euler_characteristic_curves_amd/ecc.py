@@ -335,6 +335,30 @@ def ecc_soft_bwd_tau_batched(grids, tau, lam, grad_out, grad_tau=None, ws=None):
     return grad_tau
 
 
+def ecc_soft_bwd_tau_shared(grids, tau, lam, grad_out, grad_tau=None, ws=None):
+    """dL/dtau of one threshold array shared by a batch, summed over the batch on
+    the device: float32[H] (see include/ecc.h)."""
+    B, H, ts, shp = _batch_args(grids, tau)
+    if ts != 0:
+        raise ValueError("tau must be one [H] array shared by the batch")
+    _dev_tensor(grad_out, "grad_out", torch.float32, grids.device)
+    if tuple(grad_out.shape) != (B, H):
+        raise ValueError("grad_out must be [B, H]")
+    if grad_tau is None:
+        grad_tau = torch.empty(H, dtype=torch.float32, device=grids.device)
+    _dev_tensor(grad_tau, "grad_tau", torch.float32, grids.device)
+    if tuple(grad_tau.shape) != (H,):
+        raise ValueError("grad_tau must be [H]")
+    s = _stream(grids)
+    nb = workspace_bytes_batched(_lib.ECC_OP_SOFT_BWD, B, H)
+    ws = get_workspace(nb, grids.device, s) if ws is None else ws
+    check(lib.ecc_soft_bwd_tau_shared(_ptr(grids), grids.dim() - 1, ctypes.cast(shp, ctypes.c_void_p), B,
+                                      _ptr(tau), H, float(lam), _ptr(grad_out), _ptr(grad_tau), _ptr(ws),
+                                      ws.numel() * ws.element_size(), s.cuda_stream),
+          "ecc_soft_bwd_tau_shared")
+    return grad_tau
+
+
 def ecc_soft_bwd_grid_batched(grids, tau, lam, grad_out, grad_grid=None):
     """dL/dgrids of a batch, float32 of the grids' shape (see include/ecc.h)."""
     B, H, ts, shp = _batch_args(grids, tau)
@@ -373,9 +397,10 @@ class SoftECCBatched(torch.autograd.Function):
         if ctx.needs_input_grad[0]:
             g_grid = ecc_soft_bwd_grid_batched(grids, tau_c, ctx.lam, grad_out)
         if ctx.needs_input_grad[1]:
-            g_tau = ecc_soft_bwd_tau_batched(grids, tau_c, ctx.lam, grad_out)
-            if tau.dim() == 1:
-                g_tau = g_tau.sum(0)  # one threshold array shared by every grid
+            if tau.dim() == 1:  # one threshold array shared by every grid: summed on the device
+                g_tau = ecc_soft_bwd_tau_shared(grids, tau_c, ctx.lam, grad_out)
+            else:
+                g_tau = ecc_soft_bwd_tau_batched(grids, tau_c, ctx.lam, grad_out)
         return g_grid, g_tau, None
 
 

@@ -206,6 +206,25 @@ int ecc_soft_bwd_tau_batched(const float* grid, int32_t ndim, const int64_t* sha
                              const float* tau, int64_t tau_stride, int32_t H, float lambda,
                              const float* grad_out, float* grad_tau, void* ws, size_t ws_bytes,
                              void* stream);
+/*
+ * dL/dtau of thresholds shared by a whole batch: grid_tau[k] =
+ *   sum over b of grad_out[b][k] * lambda * sum_{c in grid b} (-1)^dim(c) s(x)(1 - s(x)),
+ * the gradient of the one threshold array every grid of the batch uses (the
+ * batched differentiable layer with a learnable tau, section "Limitations and
+ * outlook" of the page: batched execution).  Same arguments as
+ * ecc_soft_bwd_tau_batched with tau_stride = 0, except
+ *   grad_out  device float32[batch][H]
+ *   grad_tau  device float32[H]: OVERWRITTEN with the sum over the batch.
+ * The sum is formed on the device in a fixed order (each grid's float64
+ * values, summed in grid order within groups of 64 grids, then over the
+ * groups in order), so the result does not depend on scheduling.  Workspace:
+ * ecc_workspace_bytes_batched(ECC_OP_SOFT_BWD, batch, H) bytes, zero-filled
+ * convention as above.  One kernel launch per 65535 grids.
+ */
+int ecc_soft_bwd_tau_shared(const float* grid, int32_t ndim, const int64_t* shape, int64_t batch,
+                            const float* tau, int32_t H, float lambda, const float* grad_out, float* grad_tau,
+                            void* ws, size_t ws_bytes, void* stream);
+
 int ecc_soft_bwd_grid_batched(const float* grid, int32_t ndim, const int64_t* shape, int64_t batch,
                               const float* tau, int64_t tau_stride, int32_t H, float lambda,
                               const float* grad_out, float* grad_grid, void* stream);

@@ -28,7 +28,7 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
         "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
         "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
-        "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_grid_batched",
+        "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_tau_shared", "ecc_soft_bwd_grid_batched",
         "ecc_height", "ecc_height_bwd", "ecc_height_workspace_bytes",
         "ecc_workspace_bytes", "ecc_workspace_bytes_batched", "ecc_status_string", "ecc_last_error",
         "ecc_version"])
@@ -176,7 +176,7 @@ def test_soft_grid_argument_errors(L):
     assert soft_grid(L, H=8193) == L.ECC_E_NTHRESH
 
 
-@pytest.mark.parametrize("which", ["fwd", "bwd_tau", "bwd_grid"])
+@pytest.mark.parametrize("which", ["fwd", "bwd_tau", "bwd_tau_shared", "bwd_grid"])
 def test_soft_batched_argument_errors(L, which):
     def call(B=2, ts=0, H=4, lam=1.0, ws=FAKE, wsb=1 << 40, gout=FAKE, shape=(4, 4, 4), grid=FAKE):
         arr = (ctypes.c_int64 * len(shape))(*shape)
@@ -186,6 +186,10 @@ def test_soft_batched_argument_errors(L, which):
         if which == "bwd_tau":
             return L.lib.ecc_soft_bwd_tau_batched(grid, len(shape), sp, B, FAKE, ts, H, lam, gout, FAKE, ws, wsb,
                                                   None)
+        if which == "bwd_tau_shared":  # no tau_stride: the thresholds are shared
+            if ts < 0:
+                return L.ECC_E_SHAPE
+            return L.lib.ecc_soft_bwd_tau_shared(grid, len(shape), sp, B, FAKE, H, lam, gout, FAKE, ws, wsb, None)
         return L.lib.ecc_soft_bwd_grid_batched(grid, len(shape), sp, B, FAKE, ts, H, lam, gout, FAKE, None)
     assert call(grid=None) == L.ECC_E_NULL
     assert call(B=0) == L.ECC_E_SHAPE

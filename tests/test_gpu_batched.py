@@ -240,3 +240,76 @@ def test_soft_batched_autograd(E):
     tau2 = torch.tensor(np.stack([W.tau_linspace(0, 1, 48)] * B)).cuda().requires_grad_(True)
     E.soft_ecc_batched(g.detach(), tau2, 30.0).sum().backward()
     assert tuple(tau2.grad.shape) == (B, 48)
+
+
+# ------------------------------------------- shared thresholds, summed
+@pytest.mark.parametrize("B", [1, 2, 63, 64, 65, 130, 200])
+@pytest.mark.parametrize("shape", [(9, 11), (5, 6, 7)])
+def test_soft_bwd_tau_shared(E, B, shape):
+    """dL/dtau of thresholds shared by the batch, summed on the device (groups
+    of 64 grids, then the groups): the sum of the oracle's per-grid values.
+    Repeated calls give the same bits and leave the workspace zero."""
+    import torch
+    rng = np.random.default_rng(zlib.crc32(repr(("shared", B, shape)).encode()))
+    g = rng.random((B,) + shape, dtype=np.float32)
+    tau = W.tau_linspace(-0.05, 1.05, 96)
+    gout = rng.standard_normal((B, 96)).astype(np.float32)
+    lam = 35.0
+    ws = torch.zeros(E.workspace_bytes_batched(2, B, 96), dtype=torch.uint8, device="cuda")
+    banner("soft bwd tau shared", B, shape)
+    dg, dt, dgo = _dev(g), _dev(tau), _dev(gout)
+    a = E.ecc_soft_bwd_tau_shared(dg, dt, lam, dgo, ws=ws)
+    b = E.ecc_soft_bwd_tau_shared(dg, dt, lam, dgo, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert int(torch.count_nonzero(ws).item()) == 0
+    want = sum(oracle.ecc_soft_bwd_tau(g[i], tau, lam, gout[i]) for i in range(B))
+    bad, worst = soft_close(a.cpu().numpy(), want)
+    assert bad.size == 0, worst
+
+
+def test_soft_bwd_tau_shared_more_than_one_launch(E):
+    """70000 tiny grids (two launches, 1094 groups of 64) drawn from 4096
+    distinct grids, each batch entry with its own upstream gradient.  The sum
+    is linear in g, so the oracle's value is sum_p lambda A_p (sum of g_b over
+    the entries b holding grid p), with lambda A_p = ecc_soft_bwd_tau(p, g = 1).
+    (Repeating a few grids thousands of times would multiply one grid's
+    float32 rounding by the repeat count, which is no property of the sum.)"""
+    import torch
+    rng = np.random.default_rng(251)
+    P, B = 4096, 70000
+    proto = rng.random((P, 2, 3), dtype=np.float32)
+    which = rng.integers(0, P, B)
+    g = proto[which]
+    tau = W.tau_linspace(0, 1, 16)
+    gout = rng.standard_normal((B, 16)).astype(np.float32)
+    banner("soft bwd tau shared 70000")
+    got = E.ecc_soft_bwd_tau_shared(_dev(g), _dev(tau), 20.0, _dev(gout))
+    torch.cuda.synchronize()
+    G = np.zeros((P, 16))
+    np.add.at(G, which, gout.astype(np.float64))
+    ones = np.ones(16, np.float32)
+    want = sum(G[p] * oracle.ecc_soft_bwd_tau(proto[p], tau, 20.0, ones) for p in np.unique(which))
+    bad, worst = soft_close(got.cpu().numpy(), want)
+    assert bad.size == 0, worst
+
+
+def test_soft_curves_repeat_bit_for_bit(E):
+    """Workgroup sums are formed in a fixed order and combined in fixed point:
+    repeated calls give identical bits (single grid and batch)."""
+    import torch
+    rng = np.random.default_rng(252)
+    g = _dev(rng.random((48, 50, 52), dtype=np.float32))
+    gb = _dev(rng.random((6, 20, 21, 22), dtype=np.float32))
+    tau = _dev(W.tau_linspace(0, 1, 300))
+    go = _dev(rng.standard_normal(300).astype(np.float32))
+    gob = _dev(rng.standard_normal((6, 300)).astype(np.float32))
+    banner("soft repeat bits")
+    runs = []
+    for _ in range(3):
+        runs.append([E.ecc_soft_fwd(g, tau, 40.0), E.ecc_soft_bwd_tau(g, tau, 40.0, go),
+                     E.ecc_soft_fwd_batched(gb, tau, 40.0), E.ecc_soft_bwd_tau_batched(gb, tau, 40.0, gob)])
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for x, y in zip(runs[0], r):
+            assert torch.equal(x, y)

@@ -95,11 +95,24 @@ def test_hard_directional_frame_and_box(E):
     assert np.array_equal(got.cpu().numpy(), want)
 
 
-def _moment_close(got, want, mag):
-    got, want, mag = (np.asarray(v, np.float64).ravel() for v in (got, want, mag))
-    tol = np.maximum(np.where(np.abs(want) >= 10, 1e-4 * np.abs(want), 1e-3), 1e-5 * mag)
+def _moment_close(got, want, carried):
+    """The soft tolerance of the result plus ``carried``: the error a result
+    inherits from inputs that are themselves only within a tolerance."""
+    got, want, carried = (np.asarray(v, np.float64).ravel() for v in (got, want, carried))
+    tol = np.where(np.abs(want) >= 10, 1e-4 * np.abs(want), 1e-3) + carried
     err = np.abs(got - want)
     return np.nonzero(~(err <= tol))[0], float(np.max(err / tol)) if err.size else 0.0
+
+
+def _carried_bounds(G, U, A):
+    """Bounds on the errors of dL/du and dL/dalpha when each G[d](p) may be off
+    by its soft tolerance t(p) = max(1e-3, 1e-4 |G[d](p)|): M[d, i] moves by at
+    most sum_p t(p) |p_i|, so dL/du by |alpha_d| times that and dL/dalpha by
+    sum_i |u_d,i| times that (the chain rule of height_bwd with every factor
+    replaced by its magnitude)."""
+    t = np.maximum(1e-3, 1e-4 * np.abs(np.asarray(G, np.float64)))
+    _, bu, ba = oracle.height_bwd(t, np.abs(U), np.abs(A))
+    return bu, ba
 
 
 @pytest.mark.parametrize("shape", [(1, 1), (31, 47), (130, 70), (64, 128), (1, 4), (9, 17, 33), (40, 41, 42),
@@ -117,12 +130,11 @@ def test_height_bwd(E, shape, D):
     gg2, gd2, ga2 = E.ecc_height_bwd(dG, dU, dA)
     torch.cuda.synchronize()
     wg, wd, wa = oracle.height_bwd(G, U, A)
-    _, md, ma = oracle.height_bwd(np.abs(G), np.abs(U), np.abs(A))
     bad, worst = soft_close(gg.cpu().numpy().ravel(), wg.ravel())
     assert bad.size == 0, worst
-    bad, worst = _moment_close(gd.cpu().numpy(), wd, md)
+    bad, worst = soft_close(gd.cpu().numpy().ravel(), wd.ravel())
     assert bad.size == 0, worst
-    bad, worst = _moment_close(ga.cpu().numpy(), wa, ma)
+    bad, worst = soft_close(ga.cpu().numpy().ravel(), wa.ravel())
     assert bad.size == 0, worst
     # deterministic: the same bits on a second call
     for a, b in ((gg, gg2), (gd, gd2), (ga, ga2)):
@@ -155,10 +167,12 @@ def test_soft_directional_forward_and_gradients(E, shape):
     assert bad.size == 0, ("tau", worst)
     G = np.stack([oracle.ecc_soft_bwd_grid(f[d], tau, lam, w[d]) for d in range(D)])
     wg, wd, wa = oracle.height_bwd(G, U, A)
-    _, md, ma = oracle.height_bwd(np.abs(G), np.abs(U), np.abs(A))
-    bad, worst = soft_close(dX.grad.cpu().numpy().ravel(), wg.ravel())
+    bu, ba = _carried_bounds(G, U, A)
+    # dL/dX sums the D grid gradients, each within its own soft tolerance
+    bx = np.maximum(1e-3, 1e-4 * np.abs(G)).sum(axis=0)
+    bad, worst = _moment_close(dX.grad.cpu().numpy(), wg, bx)
     assert bad.size == 0, ("grid", worst)
-    bad, worst = _moment_close(dU.grad.cpu().numpy(), wd, md)
+    bad, worst = _moment_close(dU.grad.cpu().numpy(), wd, bu)
     assert bad.size == 0, ("dirs", worst)
-    bad, worst = _moment_close(dA.grad.cpu().numpy(), wa, ma)
+    bad, worst = _moment_close(dA.grad.cpu().numpy(), wa, ba)
     assert bad.size == 0, ("alpha", worst)
