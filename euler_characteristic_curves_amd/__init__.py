@@ -10,7 +10,7 @@ an ECC entry point without the library raises ImportError.
 __version__ = "0.1.0"
 
 _API = (
-    "ecc_hard_2d", "ecc_hard_3d", "ecc_hard", "ecc_hard_batched", "ecc_soft_fwd", "ecc_soft_bwd_tau",
+    "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_3d_static", "ecc_hard", "ecc_hard_batched", "ecc_soft_fwd", "ecc_soft_bwd_tau",
     "ecc_soft_bwd_grid", "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_tau_shared",
     "ecc_soft_bwd_grid_batched",
     "workspace_bytes", "workspace_bytes_batched", "get_workspace", "EccError", "SoftECC", "soft_ecc",

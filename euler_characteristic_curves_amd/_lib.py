@@ -28,7 +28,7 @@ ECC_MAX_THRESHOLDS = 8192
 ECC_MAX_DIRECTIONS = 4096
 
 EXPORTS = (
-    "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
+    "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_3d_static", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
     "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
     "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_tau_shared", "ecc_soft_bwd_grid_batched",
     "ecc_height", "ecc_height_bwd", "ecc_height_workspace_bytes",
@@ -56,6 +56,8 @@ def _load():
     lib.ecc_hard_2d.restype = I
     lib.ecc_hard_3d.argtypes = [P, I, I64, I64, I64, P, I32, P, P, SZ, P]
     lib.ecc_hard_3d.restype = I
+    lib.ecc_hard_3d_static.argtypes = [P, I, I64, I64, I64, P, I32, P, P]
+    lib.ecc_hard_3d_static.restype = I
     lib.ecc_hard_2d_batched.argtypes = [P, I, I64, I64, I64, P, I64, I32, P, P, SZ, P]
     lib.ecc_hard_2d_batched.restype = I
     lib.ecc_hard_3d_batched.argtypes = [P, I, I64, I64, I64, I64, P, I64, I32, P, P, SZ, P]

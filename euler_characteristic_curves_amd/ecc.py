@@ -104,6 +104,23 @@ def _ptr(t):
     return t.data_ptr()  # an int: the argtypes (c_void_p) convert it
 
 
+def ecc_hard_3d_static(grid, tau, out):
+    """ecc_hard_3d on the library's static scratch array: no workspace and no
+    allocation by the library (see include/ecc.h); ``out`` is caller-owned int64[H]."""
+    _dev_tensor(grid, "grid")
+    if grid.dim() not in (2, 3):
+        raise ValueError("grid must be 2D or 3D")
+    _dev_tensor(tau, "tau", torch.float32, grid.device)
+    H = tau.numel()
+    _dev_tensor(out, "out", torch.int64, grid.device)
+    if tuple(out.shape) != (H,):
+        raise ValueError("out must be [H]")
+    dims = (1,) + tuple(grid.shape) if grid.dim() == 2 else tuple(grid.shape)
+    check(lib.ecc_hard_3d_static(_ptr(grid), _grid_dtype(grid), *dims, _ptr(tau), H, _ptr(out),
+                                 _stream(grid).cuda_stream), "ecc_hard_3d_static")
+    return out
+
+
 def ecc_hard_2d(grid, tau, out=None, ws=None):
     """Hard ECC of a 2D uint8/float32 grid: int64[H] (see include/ecc.h)."""
     _dev_tensor(grid, "grid")

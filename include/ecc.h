@@ -106,6 +106,22 @@ int ecc_hard_3d(const void* grid, int dtype, int64_t nz, int64_t ny, int64_t nx,
                 int32_t H, int64_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ecc_hard_3d without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation).  Same arguments, result and errors as ecc_hard_3d
+ * (a 2D grid is nz = 1) minus `ws` / `ws_bytes`: the workspace is a static
+ * device array inside the library, 525 KB (the ticket and accumulators of
+ * any H <= ECC_MAX_THRESHOLDS), one copy per GPU, held until the process
+ * ends.  The call allocates nothing; its first call on a device looks the
+ * array up and clears it with a kernel on `stream`, and every call leaves it
+ * zero.  All calls on one GPU share that array: calls that overlap on one GPU
+ * (other streams, other threads) race and must be serialized by the caller.
+ * A size the array cannot serve is rejected with ECC_E_WORKSPACE.
+ */
+int ecc_hard_3d_static(const void* grid, int dtype, int64_t nz, int64_t ny, int64_t nx, const float* tau,
+                       int32_t H, int64_t* out, void* stream);
+
+/*
  * Hard ECC of a batch of `batch` 2D grids of one shape, stored back to back:
  * grid[batch][ny][nx].  Grid b is binned against tau + b * tau_stride
  * (tau_stride = 0: one float32[H] threshold array for every grid; H: one row

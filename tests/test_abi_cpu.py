@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
-        "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
+        "ecc_hard_2d", "ecc_hard_3d", "ecc_hard_3d_static", "ecc_hard_2d_batched", "ecc_hard_3d_batched",
         "ecc_soft_fwd", "ecc_soft_bwd_tau", "ecc_soft_bwd_grid",
         "ecc_soft_fwd_batched", "ecc_soft_bwd_tau_batched", "ecc_soft_bwd_tau_shared", "ecc_soft_bwd_grid_batched",
         "ecc_height", "ecc_height_bwd", "ecc_height_workspace_bytes",

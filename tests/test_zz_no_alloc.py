@@ -1,0 +1,93 @@
+"""ecc_hard_3d_static (no workspace argument, a static scratch array inside
+the library) against ecc_hard_3d with a caller workspace, through the C ABI:
+bit for bit, on two calls in a row with the second input smaller, for 3D
+float, 3D uint8 and 2D (nz = 1) grids; and its size limit."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from euler_characteristic_curves_amd import workloads as W
+from tests.gpu_util import banner, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    need_gpu()
+    from euler_characteristic_curves_amd import _lib
+    return _lib
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dims(g):
+    return (1,) + tuple(g.shape) if g.dim() == 2 else tuple(g.shape)
+
+
+def _with_workspace(L, g, tau, dtype):
+    import torch
+    H = tau.numel()
+    out = torch.empty(H, dtype=torch.int64, device="cuda")
+    nb = L.lib.ecc_workspace_bytes(L.ECC_OP_HARD, 3, None, H)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    st = L.lib.ecc_hard_3d(_ptr(g), dtype, *_dims(g), _ptr(tau), H, _ptr(out), _ptr(ws), nb, s)
+    assert st == 0, L.lib.ecc_last_error()
+    return out
+
+
+def _static(L, g, tau, dtype):
+    import torch
+    H = tau.numel()
+    out = torch.empty(H, dtype=torch.int64, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    st = L.lib.ecc_hard_3d_static(_ptr(g), dtype, *_dims(g), _ptr(tau), H, _ptr(out), s)
+    assert st == 0, L.lib.ecc_last_error()
+    return out
+
+
+@pytest.mark.parametrize("kind", ["f32_3d", "u8_3d", "f32_2d"])
+def test_static_matches_workspace_call(L, kind):
+    import torch
+    rng = np.random.default_rng({"f32_3d": 900, "u8_3d": 901, "f32_2d": 902}[kind])
+    if kind == "f32_3d":
+        big, small = rng.random((70, 90, 260), dtype=np.float32), rng.random((9, 17, 33), dtype=np.float32)
+        taus = (W.tau_linspace(0, 1, 1024), W.tau_linspace(0, 1, 300))
+        dtype = L.ECC_F32
+    elif kind == "u8_3d":
+        big = rng.integers(0, 256, (64, 130, 257), dtype=np.uint8)
+        small = rng.integers(0, 256, (5, 6, 7), dtype=np.uint8)
+        taus = (W.tau_integers(256), W.tau_integers(97))
+        dtype = L.ECC_U8
+    else:
+        big, small = rng.random((1500, 1100), dtype=np.float32), rng.random((31, 47), dtype=np.float32)
+        taus = (W.tau_linspace(0, 1, 8192), W.tau_linspace(0, 1, 5))
+        dtype = L.ECC_F32
+    for g, tau in ((big, taus[0]), (small, taus[1])):
+        banner("static scratch", kind, g.shape, "H=%d" % tau.size)
+        dg = torch.from_numpy(np.ascontiguousarray(g)).cuda()
+        dt = torch.from_numpy(np.ascontiguousarray(tau)).cuda()
+        a = _static(L, dg, dt, dtype)
+        b = _with_workspace(L, dg, dt, dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), (kind, g.shape)
+
+
+def test_static_rejects_sizes_beyond_the_array(L):
+    import torch
+    g = torch.zeros((2, 3, 4), device="cuda")
+    tau = torch.zeros(8193, device="cuda")
+    out = torch.empty(8193, dtype=torch.int64, device="cuda")
+    st = L.lib.ecc_hard_3d_static(_ptr(g), L.ECC_F32, 2, 3, 4, _ptr(tau), 8193, _ptr(out), None)
+    assert st == L.ECC_E_NTHRESH
+    assert b"8193" in L.lib.ecc_last_error()
+    # nothing was enqueued: a valid call still works
+    st = L.lib.ecc_hard_3d_static(_ptr(g), L.ECC_F32, 2, 3, 4, _ptr(tau[:4]), 4, _ptr(out), None)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert out[:4].cpu().tolist() == [1, 1, 1, 1]
