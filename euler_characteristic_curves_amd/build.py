@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libecc_mi355.so")
 
-SOURCES = ["ecc_api.cpp", "ecc_hard.hip", "ecc_soft.hip", "ecc_soft_grad.hip", "ecc_height.hip"]
+SOURCES = ["ecc_api.cpp", "ecc_hard.hip", "ecc_soft.hip", "ecc_soft_grad.hip", "ecc_height.hip", "ecc_static.hip"]
 RATE_SOURCE = "ecc_sigmoid_rate.hip"
 RATE_LIB = os.path.join(PKG, "libecc_sigmoid_rate.so")
 ARCH = os.environ.get("ECC_OFFLOAD_ARCH", "gfx950")

@@ -11,7 +11,6 @@
 #include <string.h>
 
 #include <atomic>
-#include <mutex>
 
 #include "ecc_internal.hpp"
 
@@ -128,50 +127,6 @@ int hip_status(hipError_t e) {
   return fail(ECC_E_HIP, "HIP error: %s", hipGetErrorString(e));
 }
 
-// ------------------------------------------ workspace of ecc_hard_3d_static
-// The workspace of one hard call (ticket + accumulators) for any H up to
-// ECC_MAX_THRESHOLDS, as a file-scope device array: every GPU the library
-// runs on holds its own copy until the process ends.  Host code never uses
-// the array's name as an address: its device address on each device comes
-// from hipGetSymbolAddress, once per device, and is kept in g_scratch.
-constexpr size_t kScratchBytes = ecc::kWsHeader + (size_t)ecc::kAccCopies * ECC_MAX_THRESHOLDS * sizeof(long long);
-static __device__ __align__(256) unsigned char scratch[kScratchBytes];
-
-std::atomic<void*> g_scratch[kMaxDevices];
-std::mutex g_scratch_mu;
-
-__global__ void zero_scratch(unsigned long long* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0ull;
-}
-
-// Device address of this device's scratch; on the first call for a device it
-// is looked up and cleared (a fill kernel on `stream`, not a memset, so that
-// the call can be captured into a graph).
-int scratch_for_current_device(hipStream_t stream, void** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_status(e);
-  if (dev < 0 || dev >= kMaxDevices) return fail(ECC_E_HIP, "%sdevice %lld beyond the library's table", nullptr, dev);
-  void* p = g_scratch[dev].load(std::memory_order_acquire);
-  if (!p) {
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    p = g_scratch[dev].load(std::memory_order_acquire);
-    if (!p) {
-      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-      if (e != hipSuccess) return hip_status(e);
-      if (!p) return fail(ECC_E_HIP, "%shipGetSymbolAddress returned NULL for the scratch array");
-      hipLaunchKernelGGL(zero_scratch, dim3(64), dim3(256), 0, stream,
-                         reinterpret_cast<unsigned long long*>(p), kScratchBytes / sizeof(unsigned long long));
-      e = hipGetLastError();
-      if (e != hipSuccess) return hip_status(e);
-      g_scratch[dev].store(p, std::memory_order_release);
-    }
-  }
-  *out = p;
-  return ECC_OK;
-}
-
 }  // namespace
 
 namespace ecc {
@@ -216,13 +171,13 @@ int ecc_hard_3d_static(const void* grid, int dtype, int64_t nz, int64_t ny, int6
   int st = check_hard(grid, dtype, nz, ny, nx, tau, H, out, nullptr, 0, false);
   if (st != ECC_OK) return st;
   const size_t need = ecc::workspace_bytes(H);
-  if (need > kScratchBytes)
+  if (need > ecc::kStaticWorkspaceBytes)
     return fail(ECC_E_WORKSPACE, "%sH=%lld needs %lld bytes of scratch, more than the static array holds",
                 nullptr, H, (long long)need);
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   void* ws = nullptr;
-  st = scratch_for_current_device(s, &ws);
-  if (st != ECC_OK) return st;
+  const hipError_t e = ecc::static_workspace(s, &ws);
+  if (e != hipSuccess) return hip_status(e);
   ecc::HardArgs a{grid, dtype, nz, ny, nx, tau, H, out, ws};
   return hip_status(ecc::launch_hard(a, s));
 }

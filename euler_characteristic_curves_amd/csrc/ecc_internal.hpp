@@ -129,6 +129,13 @@ struct DeviceInfo {
 // Per-device properties, cached (ecc_api.cpp).
 hipError_t device_info(DeviceInfo* info);
 
+// The workspace of ecc_hard_3d_static: a static device array per GPU that
+// holds the workspace of one hard call for any H <= 8192 (ecc_static.hip).
+constexpr size_t kStaticWorkspaceBytes = kWsHeader + (size_t)kAccCopies * 8192 * sizeof(long long);
+// Its address on the current device (looked up and cleared on `stream` by
+// the first call for that device).
+hipError_t static_workspace(hipStream_t stream, void** ptr);
+
 hipError_t launch_hard(const HardArgs& a, hipStream_t stream);
 hipError_t launch_soft(const SoftArgs& a, hipStream_t stream);
 hipError_t launch_soft_grad(const GradArgs& a, hipStream_t stream);
