@@ -861,10 +861,15 @@ struct RawLut {
 // its bin): the bucket table, a per-bucket scan, or a binary search.
 // With VEC = 8 a wave would cover a whole row of up to 512 values, with no
 // neighbouring chunks and no edge values to load or bin.
+// PARTIAL (runtime, wave-uniform; vector loads only): the chunk of aligned
+// rows runs past the row end.  A lane then lies wholly inside or wholly past
+// it (rows hold whole vectors); lanes past it load the chunk's first vector
+// and carry trash keys, which also makes them the out-of-grid right
+// neighbour of the last real column.
 template <int VEC, int C, int TY, bool SCALAR, typename KEY>
 __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_t ny, int64_t nx, int64_t zs,
                                            int64_t ze, int64_t ys, int64_t xb, int lane, int lofs, int* hist,
-                                           int trash_bin, const LutBin& lb, KEY key) {
+                                           int trash_bin, const LutBin& lb, KEY key, bool partial = false) {
   static_assert(VEC == 4 || VEC == 8, "float rows are loaded as float4");
   constexpr bool EDGES = VEC == 4;
   // keys are LDS byte addresses of this lane's counters (see tele_add)
@@ -872,8 +877,10 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
   constexpr int64_t CHUNK = 64 * VEC;
   const int64_t plane = ny * nx;
   const bool has_l = xb > 0, has_r = xb + CHUNK < nx;
-  // byte offset of the vector from the element just left of the chunk
-  const unsigned int voff = 4u + 4u * VEC * (unsigned int)lane;
+  // byte offset of the vector from the element just left of the chunk (lanes
+  // past the row end of a partial chunk read lane 0's)
+  const bool lane_in = !partial || xb + (int64_t)VEC * lane < nx;
+  const unsigned int voff = 4u + 4u * VEC * (unsigned int)(lane_in ? lane : 0);
   // Edge values (the columns just outside the chunk, needed by lanes 0 and
   // 63) are loaded and binned once per plane for all TY+1 rows: lane r holds
   // row r's left edge, lane 63-r row r's right edge.  Their keys carry the
@@ -921,6 +928,9 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
       if constexpr (SCALAR) {
 #pragma unroll
         for (int j = 0; j < VEC; ++j) k[j] = cok(j) ? k[j] : trash;
+      } else if (partial) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) k[j] = lane_in ? k[j] : trash;
       }
     } else {
 #pragma unroll
@@ -1018,6 +1028,49 @@ __device__ __forceinline__ void tile3d_generic(const typename Elem<DT>::T* grid,
   }
 }
 
+// Float 3D tiles other than the hot one (bucket table with one threshold per
+// bucket, aligned rows): unaligned rows (element loads), and the per-bucket
+// scan and binary-search keys.  They walk
+// the tile's rows two at a time (each pair with its own one-row halo), which
+// keeps their live registers below the hot tile's, so the kernel's register
+// allocation is set by the hot tile and needs no spills.  (With all six
+// paths at four rows the kernel spilled 12 VGPRs and 56 SGPRs per wave, and
+// the spill code ran in the hot loop.)
+template <int VEC, int C, int TY>
+__device__ __forceinline__ void tile3d_lut_other(const float* grid, int64_t nz, int64_t ny, int64_t nx,
+                                                 int64_t zs, int64_t ze, int64_t ys, int64_t xb, int lane,
+                                                 int lofs, int* hist, int nbins, const LutBin& lb,
+                                                 const SearchBin& sb, int lut_mode, bool aligned) {
+  const bool partial = xb + 64 * VEC > nx;
+  for (int r = 0; r < TY && ys + r < ny; r += 2) {
+    const int64_t y = ys + r;
+    if (lut_mode == 1) {
+      // (only unaligned rows come here with this table)
+      auto key = [&](float v) { return lut_key(v, lb); };
+      tile3d_lut<VEC, C, 2, true>(grid, nz, ny, nx, zs, ze, y, xb, lane, lofs, hist, nbins, lb, key);
+    } else if (lut_mode == 2) {
+      // bucket of v, then the few thresholds sharing it
+      auto key = [&](float v) {
+        const float2 e = lb.lut[lut_bucket(v, lb)];
+        const int b0 = __float_as_int(e.y), c = __float_as_int(e.x);
+        int k = b0;
+        for (int i = 0; i < c; ++i) k += (int)(sb.R[b0 + i] < v);
+        return sb.base + k * sb.stride;
+      };
+      if (aligned)
+        tile3d_lut<VEC, C, 2, false>(grid, nz, ny, nx, zs, ze, y, xb, lane, lofs, hist, nbins, lb, key, partial);
+      else
+        tile3d_lut<VEC, C, 2, true>(grid, nz, ny, nx, zs, ze, y, xb, lane, lofs, hist, nbins, lb, key);
+    } else {
+      auto key = [&](float v) { return search_key(v, sb); };
+      if (aligned)
+        tile3d_lut<VEC, C, 2, false>(grid, nz, ny, nx, zs, ze, y, xb, lane, lofs, hist, nbins, lb, key, partial);
+      else
+        tile3d_lut<VEC, C, 2, true>(grid, nz, ny, nx, zs, ze, y, xb, lane, lofs, hist, nbins, lb, key);
+    }
+  }
+}
+
 // NT threads per workgroup; MINW waves per SIMD that the register budget must
 // allow (so that two 512-thread workgroups share a CU).
 template <int DT, int VEC, int C, int TY, int NT, int MINW>
@@ -1059,32 +1112,13 @@ __global__ __launch_bounds__(NT, MINW) void hard3d_kernel(HardArgs a, int nbins,
     const int64_t ze = zs + TZ < nz ? zs + TZ : nz;
     const int64_t xb = tx * CHUNK;
     if constexpr (DT == 1) {
-      const bool full = vok && xb + CHUNK <= nx;
-      if (lut_mode == 1) {
+      if (lut_mode == 1 && vok) {
         auto key = [&](float v) { return lut_key(v, lb); };
-        if (full)
-          tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
-        else
-          tile3d_lut<VEC, C, TY, true>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
-      } else if (lut_mode == 2) {
-        // bucket of v, then the few thresholds sharing it
-        auto key = [&](float v) {
-          const float2 e = lb.lut[lut_bucket(v, lb)];
-          const int b0 = __float_as_int(e.y), c = __float_as_int(e.x);
-          int k = b0;
-          for (int i = 0; i < c; ++i) k += (int)(sb.R[b0 + i] < v);
-          return sb.base + k * sb.stride;
-        };
-        if (full)
-          tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
-        else
-          tile3d_lut<VEC, C, TY, true>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
+        tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key,
+                                      xb + CHUNK > nx);
       } else {
-        auto key = [&](float v) { return search_key(v, sb); };
-        if (full)
-          tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
-        else
-          tile3d_lut<VEC, C, TY, true>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
+        tile3d_lut_other<VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, sb, lut_mode,
+                                     vok);
       }
     } else {
       if (vok && xb + CHUNK <= nx)
