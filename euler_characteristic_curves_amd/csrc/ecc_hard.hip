@@ -520,8 +520,12 @@ __host__ __device__ inline size_t lds_layout(int DT, int nbins, int C, int H, in
 
 // ------------------------------------------------------------ bucket table
 // Exact binning with one table read for float grids.  A monotone map
-//     bucket(v) = int(clamp(fma(v, mul, add), 0, n-1))
-// splits the line into n buckets.  If no two thresholds R_k share a bucket,
+//     bucket(v) = clamp(round(v * mul + add), 0, n-1)
+// splits the line into n buckets.  It is evaluated as one fma whose addend
+// carries a bias of 2^23: the sum then lies where float32 holds exactly the
+// integers, so the fma's own rounding is the round() above, the clamp is a
+// med3 with biased bounds, and the bucket is the float's bit pattern minus
+// that of 2^23 (no conversion instruction).  NaN clamps to the low bound.  If no two thresholds R_k share a bucket,
 // then for v in bucket j every R_k in an earlier bucket is < v and every R_k
 // in a later one is > v, so
 //     bin(v) = #{k : R_k < v} = base[j] + [v > thr[j]],
@@ -532,17 +536,34 @@ __host__ __device__ inline size_t lds_layout(int DT, int nbins, int C, int H, in
 // the sweep takes the checked path.
 struct LutBin {
   const float2* lut;  // (thr, LDS byte address of bin base's counters, as int bits)
-  float mul, add, hi;
+  float mul, add, hi; // add and hi carry the 2^23 bias
+  unsigned int tbase; // LDS byte address of the table minus 8 x (bit pattern of 2^23)
   int lo4, hi4;       // this lane's copy offset in bytes, and that plus one bin's stride
 };
 
+constexpr float kLutBias = 8388608.0f;        // 2^23
+constexpr unsigned int kLutBiasBits = 0x4B000000u;
+
+// Bit pattern of bias + bucket(v), in [bits(2^23), bits(2^23) + n - 1].
+__device__ __forceinline__ unsigned int lut_bits(float v, const LutBin& lb) {
+  return __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(v, lb.mul, lb.add), kLutBias, lb.hi));
+}
+
 __device__ __forceinline__ int lut_bucket(float v, const LutBin& lb) {
-  return (int)__builtin_amdgcn_fmed3f(fmaf(v, lb.mul, lb.add), 0.0f, lb.hi);
+  return (int)(lut_bits(v, lb) - kLutBiasBits);
+}
+
+typedef __attribute__((address_space(3))) const unsigned long long lds_u64;
+
+// The table entry of v's bucket, addressed with one shift-add of the bits.
+__device__ __forceinline__ float2 lut_entry(float v, const LutBin& lb) {
+  const unsigned long long w = *(lds_u64*)(size_t)(lut_bits(v, lb) * 8u + lb.tbase);
+  return make_float2(__uint_as_float((unsigned int)w), __uint_as_float((unsigned int)(w >> 32)));
 }
 
 // Key of v: the LDS byte address of this lane's counter for bin(v).
 __device__ __forceinline__ int lut_key(float v, const LutBin& lb) {
-  const float2 e = lb.lut[lut_bucket(v, lb)];
+  const float2 e = lut_entry(v, lb);
   return __float_as_int(e.y) + ((v > e.x) ? lb.hi4 : lb.lo4);
 }
 
@@ -583,9 +604,10 @@ __device__ __forceinline__ void build_lut(const float* R, int H, int n, float2* 
   }
   if (!ok) { mul = 0.0f; add = 0.0f; }
   lb.mul = mul;
-  lb.add = add;
-  lb.hi = (float)(n - 1);
+  lb.add = add + kLutBias;
+  lb.hi = kLutBias + (float)(n - 1);
   lb.lut = lut;
+  lb.tbase = (unsigned int)(size_t)(lds_u64*)lut - 8u * kLutBiasBits;
   if (threadIdx.x == 0) { flag[0] = ok ? 1 : 0; flag[1] = 1; }
   __syncthreads();
   if (!flag[0]) return;  // uniform: every thread read the same flag
@@ -645,7 +667,9 @@ __device__ __forceinline__ Lds setup_lds(unsigned char* smem, const HardArgs& a,
   fb.add = -bc.r0 * bc.scale;
   if (!(fb.add > -__builtin_inff() && fb.add < __builtin_inff())) { fb.mul = 0.0f; fb.add = 0.0f; }
   lb.lut = L.lut;
-  lb.mul = lb.add = lb.hi = 0.0f;
+  lb.mul = 0.0f;
+  lb.add = lb.hi = kLutBias;
+  lb.tbase = (unsigned int)(size_t)(lds_u64*)L.lut - 8u * kLutBiasBits;
   lb.lo4 = 4 * ((threadIdx.x & 63) & (C - 1));
   lb.hi4 = lb.lo4 + 4 * C;
   __syncthreads();
@@ -1051,7 +1075,7 @@ __device__ __forceinline__ void tile3d_lut_other(const float* grid, int64_t nz, 
     } else if (lut_mode == 2) {
       // bucket of v, then the few thresholds sharing it
       auto key = [&](float v) {
-        const float2 e = lb.lut[lut_bucket(v, lb)];
+        const float2 e = lut_entry(v, lb);
         const int b0 = __float_as_int(e.y), c = __float_as_int(e.x);
         int k = b0;
         for (int i = 0; i < c; ++i) k += (int)(sb.R[b0 + i] < v);
@@ -1114,8 +1138,10 @@ __global__ __launch_bounds__(NT, MINW) void hard3d_kernel(HardArgs a, int nbins,
     if constexpr (DT == 1) {
       if (lut_mode == 1 && vok) {
         auto key = [&](float v) { return lut_key(v, lb); };
-        tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key,
-                                      xb + CHUNK > nx);
+        if (xb + CHUNK <= nx)
+          tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key);
+        else
+          tile3d_lut<VEC, C, TY, false>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, key, true);
       } else {
         tile3d_lut_other<VEC, C, TY>(grid, nz, ny, nx, zs, ze, ys, xb, lane, lofs, L.hist, nbins, lb, sb, lut_mode,
                                      vok);

@@ -13,10 +13,13 @@ lane-neighbour moves, the four row sequences of the telescoped decomposition
 and its weight formula ((d >> 24) of the neighbour differences), and adds the
 weights into a model of the LDS histogram.  Binning follows the kernel's
 bucket table (one threshold per bucket, or up to 8 scanned) or its binary
-search, with the same float32 bucket map.  Loads: 'full' chunks, 'scalar'
-(element loads of unaligned rows, clamped columns) and 'partial' (vector
-loads of aligned rows past the row end: lanes past it carry trash keys).
+search, with the same float32 bucket map (the 2^23-biased fma rounding).
+Loads: 'full' chunks, 'scalar' (element loads of unaligned rows, clamped
+columns) and 'partial' (vector loads of aligned rows past the row end: lanes
+past it carry trash keys).
 """
+from fractions import Fraction
+
 import numpy as np
 
 F32 = np.float32
@@ -39,11 +42,26 @@ def build_lut(R, n):
     if not ok:
         return None
 
+    # The kernel evaluates fma(v, mul, add + 2^23) in float32: between 2^23
+    # and 2^24 float32 holds exactly the integers, so the fma's single
+    # rounding is round-half-even of v * mul + add_b - 2^23; med3 then clamps
+    # to [0, n - 1] (NaN to 0) and the bucket is read from the bit pattern.
+    bias = 2.0 ** 23
+    add_b = F32(np.float64(add) + bias)   # float32 add + 2^23 (exact in float64)
+
     def bucket(v):
-        # (int)fmed3(fma(v, mul, add), 0, n-1): fma in float64 then rounded once
-        x = F32(np.float64(v) * np.float64(mul) + np.float64(add))
-        x = min(max(x, F32(0)), F32(n - 1)) if not np.isnan(x) else F32(0)
-        return int(x)
+        v = float(v)
+        if np.isnan(v):
+            return 0
+        if np.isinf(v):
+            return n - 1 if (v > 0) == (float(mul) > 0) and mul != 0 else 0
+        # v * mul is exact in float64 (24 + 24 bits); the sum rounds at most
+        # once more, which can only move the final rounding on an exact
+        # float64 tie, where the exact rational decides instead
+        x = v * float(mul) + float(add_b) - bias
+        if x - np.floor(x) == 0.5:
+            x = Fraction(v) * Fraction(float(mul)) + Fraction(float(add_b)) - Fraction(bias)
+        return min(max(int(round(x)), 0), n - 1)
 
     bk = [bucket(r) for r in R]
     # per-bucket counts
@@ -103,7 +121,10 @@ def make_key(R, lut, C):
     return key, kind
 
 
-def emulate(grid, tau, TY=4, VEC=4, C=32, TZ=2, loads='auto', force_kind=None):
+def emulate(grid, tau, TY=4, VEC=4, C=32, TZ=2, loads='auto', force_kind=None, partial_ty=None):
+    """ECC of grid at tau as the tiles compute it.  partial_ty: tile height of
+    the partial chunks of aligned rows (the kernel runs them two rows at a
+    time, and full chunks TY rows at a time); None uses TY for every chunk."""
     nz, ny, nx = grid.shape
     H = tau.size
     R = running_max(tau)
@@ -126,10 +147,11 @@ def emulate(grid, tau, TY=4, VEC=4, C=32, TZ=2, loads='auto', force_kind=None):
         mode = 'full' if full else ('partial' if (aligned and loads == 'partial') else 'scalar')
         has_l, has_r = xb > 0, xb + CH < nx
         lim = min(nx - 1 - xb, CH - 1)
-        for ys in range(0, ny, TY):
+        ty = partial_ty if (mode == 'partial' and partial_ty) else TY
+        for ys in range(0, ny, ty):
             for zs in range(0, nz, TZ):
                 ze = min(zs + TZ, nz)
-                tile(grid, key, C, TY, VEC, xb, ys, zs, ze, has_l, has_r, lim, mode, trash_bin, add)
+                tile(grid, key, C, ty, VEC, xb, ys, zs, ze, has_l, has_r, lim, mode, trash_bin, add)
     # histogram by bin
     hb = np.zeros(H + 1, dtype=np.int64)
     for addr, w in hist.items():

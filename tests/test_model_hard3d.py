@@ -40,6 +40,16 @@ def test_model_matches_oracle(shape, kind, H, TY, want_kind):
     assert np.array_equal(got, oracle.ecc_hard(g, tau))
 
 
+def test_model_with_the_kernels_tile_heights():
+    """As the kernel routes them: full chunks of aligned rows in 4-row tiles,
+    the partial chunk of each row in 2-row tiles (rows 300 and 600 long)."""
+    for shape in ((3, 9, 300), (2, 7, 600)):
+        g, tau = _case(shape, "lin", 128)
+        got, k = M.emulate(g, tau, TY=4, TZ=2, loads="partial", partial_ty=2)
+        assert k == "lut1"
+        assert np.array_equal(got, oracle.ecc_hard(g, tau))
+
+
 def test_model_on_the_unaligned_duplicated_threshold_grid():
     """5 x 300 x 257 float32 with 256 duplicated thresholds, drawn as the GPU
     random-shape parity test draws them: the element-load tile with the
