@@ -146,6 +146,38 @@ def test_hard_threshold_spacings_3d(E):
         _check_hard(E, g, tau, "3d-" + name)
 
 
+def test_hard_bucket_map_offsets_3d(E):
+    """Float 3D binning where the bucket map is least comfortable: values far
+    from zero in a narrow band (the map's offset is large next to its range),
+    a range of a few ulps, values at the bucket boundaries of linspace
+    thresholds (threshold values themselves and their float neighbours), and
+    magnitudes near the float limits."""
+    rng = np.random.default_rng(41)
+    shape = (9, 21, 300)
+    cases = []
+    for offset, width in ((1e6, 1.0), (-3e7, 64.0), (1.0, 1e-6), (5e4, 1e-2), (-1e-30, 1e-33)):
+        g = (offset + width * rng.random(shape)).astype(np.float32)
+        vals = np.unique(g)
+        # distinct thresholds: every value of a coarse band, else evenly spaced
+        tau = vals if vals.size <= 300 else W.tau_linspace(float(vals[0]), float(vals[-1]), 257)
+        cases.append((f"band-{offset:g}", g, tau.astype(np.float32)))
+    # a range of a few ulps: many grid values equal, thresholds nearly equal
+    base = np.float32(1.5)
+    steps = np.nextafter(np.float32(base), np.float32(2), dtype=np.float32)
+    ulps = np.array([base, steps, np.nextafter(steps, np.float32(2), dtype=np.float32)], np.float32)
+    g = rng.choice(ulps, size=shape).astype(np.float32)
+    cases.append(("ulps", g, np.sort(rng.choice(ulps, 5)).astype(np.float32)))
+    # grid values on the thresholds and one ulp either side of them
+    tau = W.tau_linspace(-2.0, 3.0, 300)
+    near = np.concatenate([tau, np.nextafter(tau, np.float32(-np.inf)), np.nextafter(tau, np.float32(np.inf))])
+    g = rng.choice(near.astype(np.float32), size=shape).astype(np.float32)
+    cases.append(("on-thresholds", g, tau))
+    g = (rng.standard_normal(shape) * 1e37).astype(np.float32)
+    cases.append(("huge", g, W.tau_linspace(float(g.min()), float(g.max()), 200)))
+    for name, g, tau in cases:
+        _check_hard(E, g, tau, "3d-map-" + name)
+
+
 def test_hard_special_values(E):
     rng = np.random.default_rng(5)
     specials = np.array([-0.0, 0.0, 1e-45, -1e-45, 1e-38, np.inf, -np.inf, 1.0, -1.0, 3e38], np.float32)

@@ -50,6 +50,22 @@ def test_model_with_the_kernels_tile_heights():
         assert np.array_equal(got, oracle.ecc_hard(g, tau))
 
 
+@pytest.mark.parametrize("offset,width,want_kind", [
+    (1e6, 1.0, "lut1"),       # large map offset next to a range of 16 ulps
+    (-3e7, 64.0, "lut2"),     # the biased addend's rounding puts two thresholds in a bucket
+    (1.0, 1e-6, "lut1"),      # a range of a few ulps
+])
+def test_model_bucket_map_far_from_zero(offset, width, want_kind):
+    """Grids in a narrow band far from zero, with every distinct value as a
+    threshold: the 2^23-biased bucket map still bins exactly."""
+    rng = np.random.default_rng(zlib.crc32(repr((offset, width)).encode()))
+    g = (offset + width * rng.random((3, 9, 300))).astype(np.float32)
+    tau = np.unique(g).astype(np.float32)
+    got, k = M.emulate(g, tau, TY=4, TZ=2, loads="partial", partial_ty=2)
+    assert k == want_kind
+    assert np.array_equal(got, oracle.ecc_hard(g, tau))
+
+
 def test_model_on_the_unaligned_duplicated_threshold_grid():
     """5 x 300 x 257 float32 with 256 duplicated thresholds, drawn as the GPU
     random-shape parity test draws them: the element-load tile with the
