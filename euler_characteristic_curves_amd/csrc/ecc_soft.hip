@@ -360,11 +360,12 @@ hipError_t launch_soft(const SoftArgs& a, hipStream_t s) {
   int64_t g = ((int64_t)di.cus * 64 + a.batch - 1) / a.batch;
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
-  // fixed point: |partial| and |total| <= #cells <= 8 * nvox, kept below 2^61
+  // fixed point: |partial| and |total| <= #cells <= 8 * nvox, kept below 2^61;
+  // the finest resolution that allows (small grids get more fraction bits:
+  // the backward scales the sum by lambda g_k, and so its quantization)
   int bits = 0;
   while (bits < 62 && (((int64_t)1) << bits) < 8 * nvox + 8) ++bits;
-  int shift = 61 - bits;
-  if (shift > 40) shift = 40;
+  const int shift = 61 - bits;
   const size_t lds = kBlock * sizeof(long long) + 4 * sizeof(int) + kTermCap * sizeof(Term) +
                      (size_t)a.H * sizeof(double);
   auto k = a.grad_out ? soft_kernel<true> : soft_kernel<false>;

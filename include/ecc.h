@@ -151,8 +151,14 @@ int ecc_hard_3d_batched(const void* grid, int dtype, int64_t batch, int64_t nz, 
  *           sigmoid(lambda * (tau_k - value(c))), sigmoid(z) = 1/(1+exp(-z)).
  * Sigmoids are evaluated in float32 and summed in float64 per workgroup;
  * workgroup sums are combined in 64-bit fixed point (resolution 2^-s with
- * s = min(40, 61 - ceil(log2(8*voxels+8))), e.g. 2^-33 at 256^3), so the result
- * does not depend on scheduling.  One kernel launch.
+ * s = 61 - ceil(log2(8*voxels+8)), e.g. 2^-33 at 256^3), so the result
+ * does not depend on scheduling.
+ * Accuracy: |out[k] - exact| <= sum_c e_c sigmoid(x_c) + (W / 2) 2^-s
+ * + |out[k]| 2^-24, where x_c = lambda (tau_k - value(c)), e_c = (6 + 1.5 |x_c|)
+ * 2^-24 bounds the relative error of one float32 sigmoid (the exponent is
+ * formed in float32 when the thresholds span more than 100 / (lambda log2 e)
+ * either side of their middle, hence the |x_c| term), and W <= ceil(voxels /
+ * 512) is the number of workgroups on the grid.  One kernel launch.
  */
 int ecc_soft_fwd(const float* grid, int32_t ndim, const int64_t* shape, const float* tau, int32_t H,
                  float lambda, float* out, void* ws, size_t ws_bytes, void* stream);
@@ -164,7 +170,13 @@ int ecc_soft_fwd(const float* grid, int32_t ndim, const int64_t* shape, const fl
  *             grad_out[k] * lambda * sum_c (-1)^dim(c) s(x)(1 - s(x)),
  *             x = lambda * (tau_k - value(c)), s = sigmoid.
  * (out[k] depends on tau_k only, so the Jacobian is diagonal.)  Same
- * arithmetic and determinism as ecc_soft_fwd.  One kernel launch.
+ * arithmetic and determinism as ecc_soft_fwd; the sum is formed before the
+ * scaling by lambda * grad_out[k], which therefore scales its error:
+ * |grad_tau[k] - exact| <= lambda |grad_out[k]| (sum_c e_c s(x_c)(1 - s(x_c))
+ * + (W / 2) 2^-s) + |grad_tau[k]| 2^-24 with e_c = (8 + 1.5 |x_c|) 2^-24 and
+ * W, s as for ecc_soft_fwd.  Where the signed sum cancels and lambda
+ * |grad_out[k]| is large, that can exceed a fixed absolute tolerance.  One
+ * kernel launch.
  */
 int ecc_soft_bwd_tau(const float* grid, int32_t ndim, const int64_t* shape, const float* tau,
                      int32_t H, float lambda, const float* grad_out, float* grad_tau, void* ws,
