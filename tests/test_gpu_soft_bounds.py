@@ -3,10 +3,11 @@ the error bounds the ABI documents (include/ecc.h): float32 sigmoids of a few
 ulps, plus |x| ulps where the exponent is formed in float32, and the
 fixed-point combination of workgroup sums, all scaled by lambda |g_k| in the
 backward.  The cases reach far past the 1e-4 / 1e-3 tolerance regime: upstream
-gradients of a few thousand, lambda up to 2e6 over the data range, thresholds
-far outside the data, narrow and wide value ranges.  Also a regression case for
-the fixed-point resolution: a large lambda |g| on thresholds beyond the data,
-whose outputs are sums of sigmoid tails."""
+gradients of a few thousand, lambda times the data range up to 2000 (lambda
+up to 2e6 on the narrowest data), thresholds far outside the data, narrow and
+wide value ranges.  Also a regression case for the fixed-point resolution: a
+large lambda |g| on thresholds beyond the data, whose outputs are sums of
+sigmoid tails."""
 
 import numpy as np
 import pytest
