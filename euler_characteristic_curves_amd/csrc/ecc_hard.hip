@@ -848,14 +848,14 @@ __device__ __forceinline__ void tile3d_fast(const typename Elem<DT>::T* grid, in
 #undef ECC_PLANE_STEP
 }
 
-// Float interior tile with bucket-table binning (no per-value check).  The
-// wave holds the keys of TY+1 rows (TY plus the one-row y halo) of planes z
-// and z+1 and marches along z; the raw rows of plane z+2 are in flight while
-// plane z is processed.  Each lane also loads one value outside the wave's
-// column chunk: lane 0 the one on the left, every other lane the one on the
-// right (only lane 63 uses it), so one load and one binning serve both edges.
-// Row and plane validity is wave-uniform and handled by branches.  The z loop
-// is unrolled twice so that planes z and z+1 swap roles instead of being copied.
+// Float tile with bucket-table binning (tile3d_lut below).  The wave holds the
+// keys of TY+1 rows (TY plus the one-row y halo) of planes z and z+1 and
+// marches along z; the raw rows of plane z+2 are in flight while plane z is
+// processed.  The values just outside the wave's column chunk (one per row and
+// side) are loaded and binned once per plane in a few edge lanes and moved to
+// lanes 0 and 63 by DPP row shifts.  Row and plane validity is wave-uniform and
+// handled by branches.  The z loop is unrolled twice so that planes z and z+1
+// swap roles instead of being copied.
 // Compile-time loop (DPP controls must be constants).
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -885,11 +885,12 @@ struct RawLut {
 // its bin): the bucket table, a per-bucket scan, or a binary search.
 // With VEC = 8 a wave would cover a whole row of up to 512 values, with no
 // neighbouring chunks and no edge values to load or bin.
-// PARTIAL (runtime, wave-uniform; vector loads only): the chunk of aligned
-// rows runs past the row end.  A lane then lies wholly inside or wholly past
-// it (rows hold whole vectors); lanes past it load the chunk's first vector
-// and carry trash keys, which also makes them the out-of-grid right
-// neighbour of the last real column.
+// partial (wave-uniform; vector loads only): the chunk of aligned rows runs
+// past the row end.  A lane then lies wholly inside or wholly past it (rows
+// hold whole vectors); lanes past it load the chunk's first vector and carry
+// trash keys, which also makes them the out-of-grid right neighbour of the
+// last real column.  Callers pass a constant, so each call site inlines its
+// own copy and full chunks carry no per-value select.
 template <int VEC, int C, int TY, bool SCALAR, typename KEY>
 __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_t ny, int64_t nx, int64_t zs,
                                            int64_t ze, int64_t ys, int64_t xb, int lane, int lofs, int* hist,
