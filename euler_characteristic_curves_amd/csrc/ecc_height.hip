@@ -47,6 +47,13 @@ __host__ __device__ inline HeightGeom height_geom(const HeightArgs& a) {
   return g;
 }
 
+// A voxel index as float32, rounded once: through float64, which holds any
+// index exactly.  (The direct 64-bit-integer conversion that the compiler
+// emits for this target, a normalising 64-bit shift and a 32-bit convert,
+// gave wrong coordinates now and then for indices of 256 and up in the
+// element-wise kernel below; the float64 route has no 64-bit shift.)
+__device__ __forceinline__ float coord(int64_t i) { return (float)(double)i; }
+
 // Height of one voxel, rounded step by step (no contraction into FMAs).
 template <int ND>
 __device__ __forceinline__ float height_of(float X, float alpha, const float* u, float pz, float py, float px) {
@@ -90,7 +97,7 @@ __global__ __launch_bounds__(kHNT) void height_kernel(HeightArgs a) {
       float* out = a.out + (size_t)d * (size_t)g.nvox + row * g.nx;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (xs[j] < g.nx) out[xs[j]] = height_of<ND>(X[j], al, u, (float)z, (float)y, (float)xs[j]);
+        if (xs[j] < g.nx) out[xs[j]] = height_of<ND>(X[j], al, u, coord(z), coord(y), coord(xs[j]));
     }
   }
 }
@@ -143,15 +150,15 @@ __global__ __launch_bounds__(kHNT) void height_vec_kernel(HeightArgs a, int64_t 
   for (int64_t q = q0; q < nquads; q += stride, w.step()) {
     const int64_t idx = 4 * q, x0 = w.x;
     const float4 X = *reinterpret_cast<const float4*>(a.grid + idx);
-    const float pz = (float)(ND == 3 ? w.z : 0), py = (float)w.y;
+    const float pz = coord(ND == 3 ? w.z : 0), py = coord(w.y);
     for (int d = 0; d < D; ++d) {
       const float* u = sd + d * ND;
       const float al = sd[D * ND + d];
       float4 f;
-      f.x = height_of<ND>(X.x, al, u, pz, py, (float)(x0 + 0));
-      f.y = height_of<ND>(X.y, al, u, pz, py, (float)(x0 + 1));
-      f.z = height_of<ND>(X.z, al, u, pz, py, (float)(x0 + 2));
-      f.w = height_of<ND>(X.w, al, u, pz, py, (float)(x0 + 3));
+      f.x = height_of<ND>(X.x, al, u, pz, py, coord(x0 + 0));
+      f.y = height_of<ND>(X.y, al, u, pz, py, coord(x0 + 1));
+      f.z = height_of<ND>(X.z, al, u, pz, py, coord(x0 + 2));
+      f.w = height_of<ND>(X.w, al, u, pz, py, coord(x0 + 3));
       *reinterpret_cast<float4*>(a.out + (size_t)d * (size_t)nvox + idx) = f;
     }
   }

@@ -59,6 +59,43 @@ def test_heights_bit_exact(E, shape, D):
     assert same.all(), np.argwhere(~same)[:5].tolist()
 
 
+@pytest.mark.parametrize("shape", [(16, 49, 257), (9, 31, 259), (5, 17, 263), (3, 40, 299), (70, 257), (33, 1283)])
+def test_heights_are_the_coordinates(E, shape):
+    """Zero grid, alpha = 1 and unit directions: every height is a voxel
+    coordinate, an exact float32.  Rows that are not a multiple of 4 voxels
+    take the element-wise kernel, whose coordinates of 256 and more once
+    came out wrong now and then (an integer-to-float conversion); the
+    repeats give that a few chances to show."""
+    import torch
+    nd = len(shape)
+    U = np.eye(nd, dtype=np.float32)
+    A = np.ones(nd, np.float32)
+    want = np.indices(shape).astype(np.float32)
+    X = _dev(np.zeros(shape, np.float32))
+    for rep in range(4):
+        banner("height coordinates", shape, rep)
+        got = E.ecc_height(X, _dev(U), _dev(A))
+        torch.cuda.synchronize()
+        got = got.cpu().numpy()
+        bad = np.argwhere(got != want)
+        assert len(bad) == 0, (rep, bad[:5].tolist())
+
+
+@pytest.mark.parametrize("nx", [257, 258, 261, 270, 283, 299])
+def test_heights_bit_exact_rows_past_256(E, nx):
+    import torch
+    shape = (6, 23, nx)
+    X, U, A = _case(shape, 7, zlib.crc32(repr(("h256", nx)).encode()))
+    want = oracle.height_values(X, U, A)
+    dX, dU, dA = _dev(X), _dev(U), _dev(A)
+    for rep in range(3):
+        banner("heights rows past 256", shape, rep)
+        got = E.ecc_height(dX, dU, dA)
+        torch.cuda.synchronize()
+        bad = np.argwhere(got.cpu().numpy() != want)
+        assert len(bad) == 0, (rep, bad[:5].tolist())
+
+
 @pytest.mark.parametrize("shape", [(64, 96), (20, 24, 28)])
 def test_hard_directional_bit_exact(E, shape):
     import torch
