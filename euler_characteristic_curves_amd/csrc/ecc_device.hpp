@@ -33,6 +33,9 @@ __device__ __forceinline__ void agent_store(double* p, double v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Launches of at most this many workgroups per grid take one flat ticket.
+constexpr unsigned int kFlatTicketMax = 64;
+
 // Grid-wide reduction of per-workgroup rows of n int64 values, one launch.
 //
 // Every workgroup adds its non-zero values into one of `copies` int64
@@ -45,7 +48,7 @@ __device__ __forceinline__ void agent_store(double* p, double v) {
 // write back and invalidate the issuing XCD's L2 and cost far more than the
 // reduction itself when every workgroup issues them.  The last workgroup
 // returns true with the totals in `tot` (LDS, n entries) and leaves the
-// accumulators and the ticket zero for the next launch.  Integer addition is
+// accumulators and the tickets zero for the next launch.  Integer addition is
 // associative, so the totals do not depend on the order of arrival.
 template <int NT = kBlock, typename Local>
 __device__ bool grid_reduce(void* ws, int H, int n, Local local, long long* tot, int* lds_flag,
@@ -66,8 +69,32 @@ __device__ bool grid_reduce(void* ws, int H, int n, Local local, long long* tot,
   __builtin_amdgcn_s_waitcnt(0);  // this wave's atomics are acknowledged
   __syncthreads();                // ... and every other wave's of this workgroup
   if (threadIdx.x == 0) {
-    const unsigned int prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = (prev == gridDim.x - 1);
+    int last = 0;
+    if (copies == kAccCopies && gridDim.x > kFlatTicketMax) {
+      // Two-level ticket.  Atomics on one address are performed one after
+      // another at the point of coherence, and when all workgroups finish
+      // together a single ticket queues them all.  Workgroups count into
+      // one of at most kTicketGroups group tickets (each on its own line);
+      // the last of a group, having seen every member's increment (and so
+      // every member's accumulator adds performed), counts into the main
+      // ticket, whose last taker holds every contribution.
+      unsigned int* groups =
+          reinterpret_cast<unsigned int*>(reinterpret_cast<char*>(acc) + (size_t)copies * stride * sizeof(long long));
+      const unsigned int gs = (gridDim.x + kTicketGroups - 1) / kTicketGroups;
+      const unsigned int ng = (gridDim.x + gs - 1) / gs;
+      const unsigned int g = blockIdx.x / gs;
+      const unsigned int gsize = min(gs, gridDim.x - g * gs);
+      unsigned int* gt = groups + (size_t)g * (kTicketLine / sizeof(unsigned int));
+      const unsigned int p = __hip_atomic_fetch_add(gt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (p == gsize - 1) {
+        __hip_atomic_store(gt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned int q = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = (q == ng - 1);
+      }
+    } else {
+      const unsigned int prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = (prev == gridDim.x - 1);
+    }
     if (last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *lds_flag = last;
   }

@@ -179,7 +179,7 @@ __device__ __forceinline__ void flush_and_finish(const HardArgs& a, int nbins, i
   auto local = [&](int b) {
     long long s = 0;
 #pragma unroll
-    for (int c = 0; c < C; ++c) s += hist[b * C + c];
+    for (int c = 0; c < C; ++c) s += hist[b * C + ((c + (int)threadIdx.x) & (C - 1))];
     return s;
   };
   if (gridDim.x == 1) {
@@ -396,6 +396,28 @@ __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, in
     }
   };
   const bool has_l = xb > 0, has_r = xb + CHUNK < nx;
+  // Keys of a fetched row as counter addresses.  For bytes the address
+  // abase + 4C * byte is one unsigned byte dot product per value: the byte's
+  // word against a word holding 4C in that byte's place, accumulated onto
+  // abase.
+  auto keys = [&](const RawRow<DT, VEC>& raw, bool valid, auto check, int (&k)[VEC], int& kl, int& kr) {
+    if constexpr (ADDR && 4 * C <= 255 && VEC == 16) {
+      const unsigned int w[4] = {raw.v.x, raw.v.y, raw.v.z, raw.v.w};
+#pragma unroll
+      for (int j = 0; j < VEC; ++j)
+        k[j] = (int)__builtin_amdgcn_udot4(w[j >> 2], (4u * C) << (8 * (j & 3)), abase, false);
+      const int ta = (int)(abase + 4u * C * (unsigned int)trash);
+      kl = (valid && has_l) ? (int)(abase + 4u * C * (unsigned int)raw.l) : ta;
+      kr = (valid && has_r) ? (int)(abase + 4u * C * (unsigned int)raw.r) : ta;
+      if constexpr (decltype(check)::value) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) k[j] = valid ? k[j] : ta;
+      }
+    } else {
+      row_keys<DT, VEC, decltype(check)::value>(raw, valid, has_l, has_r, trash, fb, k, kl, kr);
+      to_addr(k, kl, kr);
+    }
+  };
   const int64_t xl = has_l ? xb - 1 : xb, xr = has_r ? xb + CHUNK : xb;
   const bool lane_in = !PARTIAL || xb + (int64_t)lane * VEC < nx;
   const int vlane = lane_in ? lane : 0;  // lanes past the row end load a valid vector
@@ -410,16 +432,14 @@ __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, in
     fetch_row<DT, VEC>(q1, rowp(ys + 2), xb, vlane, xl, xr);
     fetch_row<DT, VEC>(q2, rowp(ys + 3), xb, vlane, xl, xr);
     fetch_row<DT, VEC>(q3, rowp(ys + 4), xb, vlane, xl, xr);
-    row_keys<DT, VEC>(r0, lane_in, has_l, has_r, trash, fb, cur, cl, cr);
-    to_addr(cur, cl, cr);
+    keys(r0, lane_in, std::true_type{}, cur, cl, cr);
   }
   int nxt[VEC], nl, nr;
   // main loop: four rows per trip, every "next" row inside the grid, one load per
   // stage issued four rows ahead
 #define ECC_ROW2D_FAST(Q, K)                                                         \
   {                                                                                  \
-    row_keys<DT, VEC, PARTIAL>(Q, lane_in, has_l, has_r, trash, fb, nxt, nl, nr);    \
-    to_addr(nxt, nl, nr);                                                            \
+    keys(Q, lane_in, std::integral_constant<bool, PARTIAL>{}, nxt, nl, nr);           \
     fetch_row<DT, VEC>(Q, rowp(y + K + 5), xb, vlane, xl, xr);                       \
     row2d<VEC, C, ADDR>(cur, cl, cr, nxt, nl, nr, hist, lofs);                       \
     _Pragma("unroll") for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];                 \
@@ -429,8 +449,7 @@ __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, in
   // remainder: at most four rows, checked against the tile and grid ends
 #define ECC_ROW2D_TAIL(Q, K)                                                         \
   if (y + K < ye) {                                                                  \
-    row_keys<DT, VEC, true>(Q, lane_in && y + K + 1 < ny, has_l, has_r, trash, fb, nxt, nl, nr); \
-    to_addr(nxt, nl, nr);                                                            \
+    keys(Q, lane_in && y + K + 1 < ny, std::true_type{}, nxt, nl, nr);                 \
     row2d<VEC, C, ADDR>(cur, cl, cr, nxt, nl, nr, hist, lofs);                       \
     _Pragma("unroll") for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];                 \
     cl = nl;                                                                         \

@@ -17,11 +17,17 @@ constexpr int kAccCopies = 8;      // global accumulator copies of one grid, pic
 __host__ __device__ inline int acc_bins(int H) { return H > 256 ? H : 256; }
 
 // Workspace of one grid: [ticket + padding | copies x acc_bins(H) int64
-// accumulators].  All of it must be zero between calls; the last workgroup of
-// every launch leaves it zero.
+// accumulators | group tickets], the group tickets (one 128-byte line each,
+// see grid_reduce) only in the workspace of a lone grid (copies ==
+// kAccCopies).  All of it must be zero between calls; every launch leaves it
+// zero.
 constexpr size_t kWsHeader = 256;
+constexpr int kTicketGroups = 32;
+constexpr size_t kTicketLine = 128;
+constexpr size_t kGroupTicketBytes = (size_t)kTicketGroups * kTicketLine;
 inline size_t workspace_bytes(int H, int copies = kAccCopies) {
-  return kWsHeader + (size_t)copies * (size_t)acc_bins(H) * sizeof(long long);
+  return kWsHeader + (size_t)copies * (size_t)acc_bins(H) * sizeof(long long) +
+         (copies == kAccCopies ? kGroupTicketBytes : 0);
 }
 
 // Accumulator copies per grid in a batch: the workgroups of a launch are
@@ -131,7 +137,7 @@ hipError_t device_info(DeviceInfo* info);
 
 // The workspace of ecc_hard_3d_static: a static device array per GPU that
 // holds the workspace of one hard call for any H <= 8192 (ecc_static.hip).
-constexpr size_t kStaticWorkspaceBytes = kWsHeader + (size_t)kAccCopies * 8192 * sizeof(long long);
+constexpr size_t kStaticWorkspaceBytes = kWsHeader + (size_t)kAccCopies * 8192 * sizeof(long long) + kGroupTicketBytes;
 // Its address on the current device (looked up and cleared on `stream` by
 // the first call for that device).
 hipError_t static_workspace(hipStream_t stream, void** ptr);
