@@ -115,6 +115,11 @@ __device__ bool grid_reduce(void* ws, int H, int n, Local local, long long* tot,
 // Inclusive scan of n values with NT threads, each thread owning one
 // contiguous segment.  `get(i)` produces element i (called twice per
 // element), `put(i, v)` receives the inclusive scan.  `tmp` holds NT T.
+// `op` must be associative (integer adds, fmaxf).  256-thread workgroups scan
+// the segment totals within each wave by lane shuffles, then across the four
+// waves (two barriers).  512-thread workgroups (the 3D float kernel, which
+// sits at its 128-register limit: the shuffle form makes it spill) scan
+// them in LDS, two barriers per doubling step.
 template <typename T, int NT = kBlock, typename Op, typename Get, typename Put>
 __device__ void block_scan(int n, T identity, Op op, Get get, Put put, T* tmp) {
   const int t = threadIdx.x;
@@ -123,15 +128,30 @@ __device__ void block_scan(int n, T identity, Op op, Get get, Put put, T* tmp) {
   const int e = min(b + seg, n);
   T s = identity;
   for (int i = b; i < e; ++i) s = op(s, get(i));
-  tmp[t] = s;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    T v = t >= off ? tmp[t - off] : identity;
+  T run = identity;
+  if constexpr (NT <= 256) {
+    const int lane = t & 63, w = t >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const T v = __shfl_up(s, off);
+      if (lane >= off) s = op(v, s);
+    }
+    if (lane == 63) tmp[w] = s;
+    const T below = __shfl_up(s, 1);  // the scan over the lanes below this one
     __syncthreads();
-    tmp[t] = op(tmp[t], v);
+    for (int j = 0; j < w; ++j) run = op(run, tmp[j]);
+    if (lane > 0) run = op(run, below);
+  } else {
+    tmp[t] = s;
     __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+      T v = t >= off ? tmp[t - off] : identity;
+      __syncthreads();
+      tmp[t] = op(tmp[t], v);
+      __syncthreads();
+    }
+    if (t) run = tmp[t - 1];
   }
-  T run = t ? tmp[t - 1] : identity;
   for (int i = b; i < e; ++i) {
     run = op(run, get(i));
     put(i, run);
