@@ -350,12 +350,9 @@ __device__ __forceinline__ void row_keys(const RawRow<DT, VEC>& raw, bool valid,
 }
 
 // ------------------------------------------------------------------- 2D
-// Interior wave tile: the column chunk lies inside the grid and rows are
-// 16-byte aligned.  Rows ys..ye-1 are processed (row ye is the halo), with
-// two rows of loads in flight ahead of the row being processed.
-// One row step: cur/nxt keys of rows y and y+1 (lane-local), edge keys from
-// outside the chunk; two telescoped sequences (the row and the max of the two
-// rows) go to the histogram.
+// One row step of a 2D wave tile: cur/nxt keys of rows y and y+1
+// (lane-local), edge keys from outside the chunk; two telescoped sequences
+// (the row and the max of the two rows) go to the histogram.
 template <int VEC, int C, bool ADDR = false>
 __device__ __forceinline__ void row2d(const int (&cur)[VEC], int cl, int cr, const int (&nxt)[VEC], int nl,
                                       int nr, int* hist, int lofs) {
@@ -368,11 +365,8 @@ __device__ __forceinline__ void row2d(const int (&cur)[VEC], int cl, int cr, con
 }
 
 // Wave tile of aligned rows.  Rows ys..ye-1 are processed, row ye is the
-// halo.  Four rows of loads are in flight: the row loop is unrolled by 4 so
-// every load lands in a register that is consumed in place (a register copy
-// of an in-flight load would force the wave to wait for it).  Rows past the
-// grid are loaded from the last row (always a valid address) and turned into
-// trash keys.  PARTIAL: the column chunk runs past the row end (narrow grids,
+// halo.  Rows past the grid are loaded from the last row (always a valid
+// address) and turned into trash keys.  PARTIAL: the column chunk runs past the row end (narrow grids,
 // the last chunk of a row).  Aligned rows hold a whole number of lane
 // vectors, so a lane is wholly inside or wholly past the row; lanes past it
 // load the chunk's first vector and carry trash keys, which also makes them
@@ -423,51 +417,47 @@ __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, in
   const int vlane = lane_in ? lane : 0;  // lanes past the row end load a valid vector
   const T* lastrow = grid + (ny - 1) * nx;
   auto rowp = [&](int64_t y) { return y < ny ? grid + y * nx : lastrow; };
-  RawRow<DT, VEC> q0, q1, q2, q3;
+  // D rows of loads in flight.  Prefetches past the tile's halo row reload
+  // the halo row (a cache hit) instead of reading rows the tile never uses.
+  constexpr int D = 4;
+  auto ahead = [&](int64_t r) { return rowp(r < ye ? r : ye); };
+  RawRow<DT, VEC> q[D];
   int cur[VEC], cl, cr;
   {
     RawRow<DT, VEC> r0;
     fetch_row<DT, VEC>(r0, rowp(ys), xb, vlane, xl, xr);
-    fetch_row<DT, VEC>(q0, rowp(ys + 1), xb, vlane, xl, xr);
-    fetch_row<DT, VEC>(q1, rowp(ys + 2), xb, vlane, xl, xr);
-    fetch_row<DT, VEC>(q2, rowp(ys + 3), xb, vlane, xl, xr);
-    fetch_row<DT, VEC>(q3, rowp(ys + 4), xb, vlane, xl, xr);
+#pragma unroll
+    for (int K = 0; K < D; ++K) fetch_row<DT, VEC>(q[K], ahead(ys + 1 + K), xb, vlane, xl, xr);
     keys(r0, lane_in, std::true_type{}, cur, cl, cr);
   }
   int nxt[VEC], nl, nr;
-  // main loop: four rows per trip, every "next" row inside the grid, one load per
-  // stage issued four rows ahead
-#define ECC_ROW2D_FAST(Q, K)                                                         \
-  {                                                                                  \
-    keys(Q, lane_in, std::integral_constant<bool, PARTIAL>{}, nxt, nl, nr);           \
-    fetch_row<DT, VEC>(Q, rowp(y + K + 5), xb, vlane, xl, xr);                       \
-    row2d<VEC, C, ADDR>(cur, cl, cr, nxt, nl, nr, hist, lofs);                       \
-    _Pragma("unroll") for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];                 \
-    cl = nl;                                                                         \
-    cr = nr;                                                                         \
-  }
-  // remainder: at most four rows, checked against the tile and grid ends
-#define ECC_ROW2D_TAIL(Q, K)                                                         \
-  if (y + K < ye) {                                                                  \
-    keys(Q, lane_in && y + K + 1 < ny, std::true_type{}, nxt, nl, nr);                 \
-    row2d<VEC, C, ADDR>(cur, cl, cr, nxt, nl, nr, hist, lofs);                       \
-    _Pragma("unroll") for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];                 \
-    cl = nl;                                                                         \
-    cr = nr;                                                                         \
-  }
+  auto step = [&]() {
+    row2d<VEC, C, ADDR>(cur, cl, cr, nxt, nl, nr, hist, lofs);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) cur[j] = nxt[j];
+    cl = nl;
+    cr = nr;
+  };
+  // main loop: D rows per trip, every "next" row inside the grid; each
+  // stage's load is consumed in place and refilled D rows ahead (a register
+  // copy of an in-flight load would make the wave wait for it)
   int64_t y = ys;
-  for (; y + 4 <= ye && y + 4 < ny; y += 4) {
-    ECC_ROW2D_FAST(q0, 0)
-    ECC_ROW2D_FAST(q1, 1)
-    ECC_ROW2D_FAST(q2, 2)
-    ECC_ROW2D_FAST(q3, 3)
+  for (; y + D <= ye && y + D < ny; y += D) {
+#pragma unroll
+    for (int K = 0; K < D; ++K) {
+      keys(q[K], lane_in, std::integral_constant<bool, PARTIAL>{}, nxt, nl, nr);
+      fetch_row<DT, VEC>(q[K], ahead(y + K + D + 1), xb, vlane, xl, xr);
+      step();
+    }
   }
-  ECC_ROW2D_TAIL(q0, 0)
-  ECC_ROW2D_TAIL(q1, 1)
-  ECC_ROW2D_TAIL(q2, 2)
-  ECC_ROW2D_TAIL(q3, 3)
-#undef ECC_ROW2D_FAST
-#undef ECC_ROW2D_TAIL
+  // remainder: fewer than D rows, checked against the tile and grid ends
+#pragma unroll
+  for (int K = 0; K < D; ++K) {
+    if (y + K < ye) {
+      keys(q[K], lane_in && y + K + 1 < ny, std::true_type{}, nxt, nl, nr);
+      step();
+    }
+  }
 }
 
 // Any wave tile (edges, unaligned rows): element loads with bounds checks.
@@ -1023,9 +1013,12 @@ __device__ __forceinline__ void tile3d_lut(const float* grid, int64_t nz, int64_
 #pragma unroll
       for (int r = 0; r <= TY; ++r) YE[r] = trash;
     }
+    // the last step's prefetch reloads the halo plane (a cache hit) rather
+    // than read a plane the tile never uses
+    const int64_t zf = z + 2 < ze ? z + 2 : ze;
 #pragma unroll
-    for (int r = 0; r <= TY; ++r) fetch(raw[r], z + 2, r);
-    if constexpr (EDGES) fetch_edges(rawe, z + 2);
+    for (int r = 0; r <= TY; ++r) fetch(raw[r], zf, r);
+    if constexpr (EDGES) fetch_edges(rawe, zf);
     rows3d<1, VEC, C, TY, true>(X, XE, XE, Y, YE, YE, ys, ny, hist, lofs);
   };
   for (int64_t z = zs; z < ze; z += 2) {
