@@ -110,7 +110,7 @@ int ecc_hard_3d(const void* grid, int dtype, int64_t nz, int64_t ny, int64_t nx,
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid allocation).  Same arguments, result and errors as ecc_hard_3d
  * (a 2D grid is nz = 1) minus `ws` / `ws_bytes`: the workspace is a static
- * device array inside the library, 525 KB (the ticket and accumulators of
+ * device array inside the library, 529 KB (the tickets and accumulators of
  * any H <= ECC_MAX_THRESHOLDS), one copy per GPU, held until the process
  * ends.  The call allocates nothing; its first call on a device looks the
  * array up and clears it with a kernel on `stream`, and every call leaves it
