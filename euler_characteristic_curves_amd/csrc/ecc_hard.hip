@@ -176,6 +176,8 @@ template <int DT, int C, int NT>
 __device__ __forceinline__ void flush_and_finish(const HardArgs& a, int nbins, int* hist, long long* tmp,
                                                  long long* ch, int* flag, long long* tot) {
   __syncthreads();
+  // per-bin sum of the C copies, starting at a lane-dependent copy so that
+  // the lanes of a wave read different banks
   auto local = [&](int b) {
     long long s = 0;
 #pragma unroll
@@ -366,19 +368,20 @@ __device__ __forceinline__ void row2d(const int (&cur)[VEC], int cl, int cr, con
 
 // Wave tile of aligned rows.  Rows ys..ye-1 are processed, row ye is the
 // halo.  Rows past the grid are loaded from the last row (always a valid
-// address) and turned into trash keys.  PARTIAL: the column chunk runs past the row end (narrow grids,
-// the last chunk of a row).  Aligned rows hold a whole number of lane
-// vectors, so a lane is wholly inside or wholly past the row; lanes past it
-// load the chunk's first vector and carry trash keys, which also makes them
-// the out-of-grid right neighbour of the last real column.
+// address) and turned into trash keys.  PARTIAL: the column chunk runs past
+// the row end (narrow grids, the last chunk of a row).  Aligned rows hold a
+// whole number of lane vectors, so a lane is wholly inside or wholly past the
+// row; lanes past it load the chunk's first vector and carry trash keys,
+// which also makes them the out-of-grid right neighbour of the last real
+// column.
 template <int DT, int VEC, int C, bool PARTIAL = false>
 __device__ __forceinline__ void tile2d_fast(const typename Elem<DT>::T* grid, int64_t ny, int64_t nx,
                                             int64_t ys, int64_t ye, int64_t xb, int lane, int lofs,
                                             int* hist, int trash, const FastBin& fb) {
   using T = typename Elem<DT>::T;
   constexpr int64_t CHUNK = 64 * VEC;
-  // uint8 grids carry keys as LDS counter addresses (see tele_add): one
-  // shift-add per value instead of one per histogram update
+  // uint8 grids carry keys as LDS counter addresses (see tele_add): the
+  // address is formed once per value instead of once per histogram update
   constexpr bool ADDR = DT == 0;
   const unsigned int abase = (unsigned int)(size_t)(lds_int*)hist + 4u * (unsigned int)lofs;
   auto to_addr = [&](int (&k)[VEC], int& kl, int& kr) {
