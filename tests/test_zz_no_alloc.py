@@ -1,7 +1,7 @@
 """ecc_hard_3d_static (no workspace argument, a static scratch array inside
 the library) against ecc_hard_3d with a caller workspace, through the C ABI:
-bit for bit, on two calls in a row with the second input smaller, for 3D
-float, 3D uint8 and 2D (nz = 1) grids; and its size limit."""
+bit for bit, on calls in a row (large, smaller, large again) for 3D float,
+3D uint8 and 2D (nz = 1) grids; and its size limit."""
 
 import ctypes
 
@@ -68,7 +68,9 @@ def test_static_matches_workspace_call(L, kind):
         big, small = rng.random((1500, 1100), dtype=np.float32), rng.random((31, 47), dtype=np.float32)
         taus = (W.tau_linspace(0, 1, 8192), W.tau_linspace(0, 1, 5))
         dtype = L.ECC_F32
-    for g, tau in ((big, taus[0]), (small, taus[1])):
+    # the large grids take the two-level ticket: the third call finds out
+    # whether the first left its group lines zero
+    for g, tau in ((big, taus[0]), (small, taus[1]), (big, taus[0])):
         banner("static scratch", kind, g.shape, "H=%d" % tau.size)
         dg = torch.from_numpy(np.ascontiguousarray(g)).cuda()
         dt = torch.from_numpy(np.ascontiguousarray(tau)).cuda()
