@@ -34,8 +34,9 @@ Pinning status (what checks this oracle against something other than itself):
                                frame (0, 1, 0) by brute force, central finite
                                differences of the whole soft pipeline in u,
                                alpha and the grid.
-  * at the 256^3 soft size the only check is the per-cell vs grouped
-    agreement of this same oracle: parity unpinned beyond that.
+  * at the 256^3 soft size: the forward and the threshold backward of a
+    256^3 checkerboard against their two-term closed form (every edge,
+    square and cube takes the high value, the box has chi = 1).
 """
 
 from .ecc import (  # noqa: F401

@@ -257,6 +257,28 @@ def test_soft_constant_grid_closed_form():
     np.testing.assert_allclose(oracle.ecc_soft(g, tau, lam), want, rtol=1e-13, atol=1e-14)
 
 
+def test_soft_checkerboard_closed_form_at_256cube():
+    """The soft curves at the 256^3 soft workload's size, pinned to a closed
+    form: on a 3D checkerboard every edge, square and cube holds both
+    parities, so all of them take the high value b, while half the vertices
+    take the low value a; the complex of a box is contractible (chi = 1), so
+    S(tau) = (n^3/2) s(l (tau - a)) + (1 - n^3/2) s(l (tau - b)) and dS/dtau
+    is l times the same sum of s (1 - s)."""
+    n, a, b, lam = 256, 0.25, 0.75, 50.0
+    g = np.where(np.indices((n, n, n)).sum(0) % 2 == 0, a, b).astype(np.float32)
+    tau = np.linspace(0, 1, 33).astype(np.float32)
+    t = tau.astype(np.float64)
+    half = n ** 3 // 2
+    sig = lambda z: 1.0 / (1.0 + np.exp(-z))
+    sa, sb = sig(lam * (t - a)), sig(lam * (t - b))
+    want = half * sa + (1 - half) * sb
+    np.testing.assert_allclose(oracle.ecc_soft(g, tau, lam), want, rtol=1e-12, atol=1e-9)
+    gout = np.linspace(-2, 3, t.size).astype(np.float32)
+    dsig = lambda z: np.exp(-np.abs(z)) / (1.0 + np.exp(-np.abs(z))) ** 2   # s (1 - s) without 1 - s
+    want_bwd = gout.astype(np.float64) * lam * (half * dsig(lam * (t - a)) + (1 - half) * dsig(lam * (t - b)))
+    np.testing.assert_allclose(oracle.ecc_soft_bwd_tau(g, tau, lam, gout), want_bwd, rtol=1e-12, atol=1e-9)
+
+
 def test_soft_large_lambda_is_hard():
     rng = np.random.default_rng(81)
     for ndim in (2, 3):
