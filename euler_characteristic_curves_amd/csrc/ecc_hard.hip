@@ -77,12 +77,16 @@ __device__ __forceinline__ void load_keys(const typename Elem<DT>::T* row, int64
   }
   if (vec_ok && x0 + VEC <= nx) {
     if constexpr (DT == 0) {
-      static_assert(VEC == 16 || VEC == 8, "u8 vector width");
+      static_assert(VEC == 16 || VEC == 8 || VEC == 4, "u8 vector width");
       if constexpr (VEC == 16) {
         const uint4 w = *reinterpret_cast<const uint4*>(row + x0);
         const unsigned int ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int j = 0; j < 16; ++j) k[j] = (int)((ws[j >> 2] >> (8 * (j & 3))) & 0xffu);
+      } else if constexpr (VEC == 4) {
+        const unsigned int w = *reinterpret_cast<const unsigned int*>(row + x0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) k[j] = (int)((w >> (8 * j)) & 0xffu);
       } else {
         const uint2 w = *reinterpret_cast<const uint2*>(row + x0);
         const unsigned int ws[2] = {w.x, w.y};
@@ -246,6 +250,7 @@ __device__ __forceinline__ void setup_bins(const HardArgs& a, float* R, float* s
 template <int DT, int VEC> struct RawRow;
 template <> struct RawRow<0, 16> { uint4 v; uint8_t l, r; };
 template <> struct RawRow<0, 8> { uint2 v; uint8_t l, r; };
+template <> struct RawRow<0, 4> { unsigned int v; uint8_t l, r; };
 template <> struct RawRow<1, 4> { float4 v; float l, r; };
 
 // Loads are unconditional: callers clamp the row pointer to a valid row and
@@ -270,6 +275,7 @@ __device__ __forceinline__ void fetch_row(RawRow<DT, VEC>& raw, const typename E
   const unsigned int off = (unsigned int)lane * (unsigned int)(VEC * sizeof(T));
   if constexpr (DT == 0 && VEC == 16) raw.v = *reinterpret_cast<const uint4*>(base + off);
   if constexpr (DT == 0 && VEC == 8) raw.v = *reinterpret_cast<const uint2*>(base + off);
+  if constexpr (DT == 0 && VEC == 4) raw.v = *reinterpret_cast<const unsigned int*>(base + off);
   if constexpr (DT == 1) raw.v = *reinterpret_cast<const float4*>(base + off);
   raw.l = row[xl];
   raw.r = row[xr];
@@ -312,7 +318,8 @@ __device__ __forceinline__ void row_keys(const RawRow<DT, VEC>& raw, bool valid,
   if constexpr (DT == 0) {
     unsigned int w[VEC / 4];
     if constexpr (VEC == 16) { w[0] = raw.v.x; w[1] = raw.v.y; w[2] = raw.v.z; w[3] = raw.v.w; }
-    else { w[0] = raw.v.x; w[1] = raw.v.y; }
+    else if constexpr (VEC == 8) { w[0] = raw.v.x; w[1] = raw.v.y; }
+    else { w[0] = raw.v; }
 #pragma unroll
     for (int j = 0; j < VEC; ++j) k[j] = (int)((w[j >> 2] >> (8 * (j & 3))) & 0xffu);
     kl = (int)raw.l;
@@ -1388,6 +1395,11 @@ hipError_t launch_hard(const HardArgs& a, hipStream_t s) {
     // 16 histogram copies: 8 measured slower (bank conflicts), 32 spend more
     // time summing the copies at the flush
     if (a.nz == 1) return launch2d<0, 16, 16, 16>(a, 256, s, di);
+    // 8 bytes per lane when every 512-byte column chunk is full, else 4: the
+    // cold tile takes partial chunks, and 256-byte chunks leave fewer of them
+    // (512x256x256: 79 -> 35 us, 256x512x768: 152 -> 96 us; 512^3: 92 against
+    // 107 us with 4 bytes per lane)
+    if (a.nx % 512 != 0) return launch3d<0, 4, 32, 4, kBlock, 1>(a, 256, s, di);
     return launch3d<0, 8, 32, 4, kBlock, 1>(a, 256, s, di);
   }
   const int nbins = a.H;
