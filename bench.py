@@ -417,7 +417,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the ECC of "
-              "one grid is a single-GPU job; the sharding design is described in DESIGN.md.",
+              "one grid is a single-GPU job, and sharding a grid over several GPUs is not built.",
               file=sys.stderr)
         sys.exit(2)
 
