@@ -33,7 +33,8 @@ __device__ __forceinline__ void agent_store(double* p, double v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Launches of at most this many workgroups per grid take one flat ticket.
+// Launches of at most this many workgroups per grid take one flat ticket
+// (callers may raise it: see flush_and_finish).
 constexpr unsigned int kFlatTicketMax = 64;
 
 // Grid-wide reduction of per-workgroup rows of n int64 values, one launch.
@@ -52,7 +53,7 @@ constexpr unsigned int kFlatTicketMax = 64;
 // associative, so the totals do not depend on the order of arrival.
 template <int NT = kBlock, typename Local>
 __device__ bool grid_reduce(void* ws, int H, int n, Local local, long long* tot, int* lds_flag,
-                            int copies = kAccCopies) {
+                            int copies = kAccCopies, unsigned int flat_max = kFlatTicketMax) {
   if (gridDim.x == 1) {  // a lone workgroup holds the totals already (tot must not alias local's data)
     for (int b = threadIdx.x; b < n; b += NT) tot[b] = local(b);
     __syncthreads();
@@ -70,7 +71,7 @@ __device__ bool grid_reduce(void* ws, int H, int n, Local local, long long* tot,
   __syncthreads();                // ... and every other wave's of this workgroup
   if (threadIdx.x == 0) {
     int last = 0;
-    if (copies == kAccCopies && gridDim.x > kFlatTicketMax) {
+    if (copies == kAccCopies && gridDim.x > flat_max) {
       // Two-level ticket.  Atomics on one address are performed one after
       // another at the point of coherence, and when all workgroups finish
       // together a single ticket queues them all.  Workgroups count into

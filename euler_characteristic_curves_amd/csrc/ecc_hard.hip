@@ -202,7 +202,11 @@ __device__ __forceinline__ void flush_and_finish(const HardArgs& a, int nbins, i
       if (b < nbins) tot[b] = v;
       __syncthreads();
     }
-  } else if (!grid_reduce<NT>(a.ws, a.H, nbins, local, tot, flag, a.acc_copies)) {
+  } else if (!grid_reduce<NT>(a.ws, a.H, nbins, local, tot, flag, a.acc_copies,
+                                 // float 2D workgroups finish spread out by their
+                                 // binning: one ticket up to 256 of them measured
+                                 // 0.3-0.45 us faster; uint8 ones finish together
+                                 DT == 1 && NT == kBlock ? 256u : kFlatTicketMax)) {
     return;
   }
   int64_t* out = a.out;
