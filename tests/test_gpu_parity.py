@@ -60,7 +60,7 @@ def _taus(rng, g, H, kind):
 SHAPES_2D = [(1, 1), (1, 7), (7, 1), (5, 13), (33, 100), (64, 1024), (130, 257), (17, 1500),
              (300, 2049), (256, 4096), (1000, 129), (3, 5000)]
 SHAPES_3D = [(1, 1, 1), (1, 5, 7), (2, 3, 4), (9, 17, 33), (20, 30, 300), (64, 64, 64), (5, 300, 257),
-             (40, 1, 1), (3, 2, 1100), (70, 9, 260)]
+             (40, 1, 1), (3, 2, 1100), (70, 9, 260), (6, 7, 768)]
 
 
 @pytest.mark.parametrize("shape", SHAPES_2D + SHAPES_3D)
